@@ -1,0 +1,150 @@
+/*
+ * libmla -- latent-space Multi-head Latent Attention (MLA) decode for AMD Instinct
+ * MI355X (gfx950). C ABI.
+ *
+ * What is computed. Page "Mla Analysis", section "Absorption Trick (FlashMLA)": the
+ * score of a query against a decompressed key Z W_k equals the absorbed query
+ * Qz = Q W_k^T against the latent row Z, and softmax(A)(Z W_v) = (softmax(A) Z) W_v,
+ * so decode works on latent rows only and leaves the W_v decompression to a separate
+ * kernel. For query row (sequence i, query token j, head e) with absorbed query
+ * Qz[576] = [q_nope W_k^T (512) | q_rope (64)] and the sequence's cached latent rows
+ * Z[u, 576] = [c_KV (512) | k_rope (64)] (section "Tensor Shapes": Z is [B, T, K],
+ * KPE is [B, T, P]; here one 576-wide row), for the visible keys u:
+ *
+ *     a_u  = softmax_scale * sum_c Qz[c] * Z[u, c]
+ *     lse  = log(sum_u exp(a_u))                       (natural log)
+ *     out  = sum_u exp(a_u - lse) * Z[u, 0:512]        (normalised O_latent)
+ *
+ * Visible keys: all u < t_i; with causal != 0 and s_q > 1, query token j sees
+ * u <= t_i - s_q + j (t_i counts the s_q new tokens, whose rows are already cached).
+ * No visible key: out = 0, lse = -inf.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument named as device memory is caller-owned device memory.
+ *    The library allocates nothing, keeps no pointer after a call returns, and
+ *    enqueues all work on `stream` (a hipStream_t; NULL = the default stream). A call
+ *    that returns MLA_OK has *enqueued* its work; device faults surface at the caller's
+ *    next synchronisation. Buffers must stay valid until that work completes.
+ *  - Every host-checkable error is returned before any work is enqueued, and then no
+ *    output is written. mla_last_error_message() gives the reason (thread-local).
+ *  - The cache is paged: 64 tokens per page. block_table[i, r] names the physical page
+ *    holding tokens 64r .. 64r+63 of sequence i.
+ *  - Device-resident preconditions the library cannot check on the host:
+ *    0 <= seqlens[i] <= max_pages * 64 and block_table[i, r] in [0, num_pages) for
+ *    r < ceil(seqlens[i] / 64). A page id outside [0, num_pages) reads as zeros
+ *    (never faults); a length above max_pages * 64 reads only max_pages pages.
+ */
+#ifndef LIBMLA_H
+#define LIBMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+/* Status codes returned by every entry point that can fail. */
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,          /* null pointer, bad size, bad enum, misalignment */
+  MLA_ERR_UNSUPPORTED = 2,          /* a shape outside the supported set (see each call) */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3,  /* plan_bytes or workspace_bytes below the required size */
+  MLA_ERR_HIP = 4,                  /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_INTERNAL = 5
+} mla_status;
+
+/* Storage of the latent cache.
+ * MLA_KV_BF16: kv_cache is bf16 [num_pages, 64, 576], a token row = 512 c_KV then 64 rope.
+ * MLA_KV_FP8_E4M3: kv_cache is bytes [num_pages, 64, 640]; a token row = 512 OCP e4m3fn
+ *   codes of c_KV then the 64 rope channels as bf16 (128 bytes); kv_scales is float32
+ *   [num_pages, 64, 4] and c_KV[c] = e4m3fn(code[c]) * scale[token, c / 128]. (FlashMLA-2
+ *   newsletter page, section "Architectural Analysis": an FP8 cache scaled up to bf16
+ *   in registers before the matrix products.) */
+typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_dtype;
+
+/* Returns MLA_ABI_VERSION of the built library. */
+int32_t mla_abi_version(void);
+
+/* Static string naming a status code ("MLA_OK", ...); "unknown status" otherwise. */
+const char* mla_status_string(int32_t status);
+
+/* Detail of the last error returned on the calling thread ("" if none). The pointer
+ * stays valid until the next libmla call on this thread. */
+const char* mla_last_error_message(void);
+
+/* Number of compute units of HIP device `device` (256 on MI355X): the natural
+ * num_workers for the calls below. Returns -1 (and sets the error message) if the
+ * device cannot be queried. */
+int32_t mla_default_num_workers(int32_t device);
+
+/* Bytes of the plan buffer mla_get_split_plan writes for this shape, or 0 if the shape
+ * is invalid or unsupported (see mla_get_split_plan). */
+size_t mla_plan_bytes(int32_t batch, int32_t s_q, int32_t heads, int32_t num_workers);
+
+/* Bytes of the workspace mla_decode_fwd needs for partial results of split sequences
+ * (an upper bound over every length mix), or 0 if the shape is invalid. */
+size_t mla_workspace_bytes(int32_t batch, int32_t s_q, int32_t heads, int32_t num_workers);
+
+/* Split-KV plan for one decode step (FlashMLA-2 newsletter page, section "Architectural
+ * Analysis": a radix-sorted scheduler that balances sequence partitions across compute
+ * units so that short and very long sequences in one batch leave no stragglers).
+ *
+ * Work items are (sequence, 128-row tile of the s_q*heads query rows). Items are sorted
+ * by page count, longest first (stable), laid end to end with a fixed per-item overhead
+ * in page units, and cut into num_workers contiguous runs of equal cost; an item cut
+ * across runs is "split" and its runs are merged by log-sum-exp in mla_decode_fwd.
+ * Runs entirely on the device (one work-group); no host synchronisation.
+ *
+ * seqlens   device int32 [batch]: cached tokens per sequence (incl. the s_q new ones).
+ * batch     1 .. 16384; batch * ceil(s_q*heads/128) must be <= 16384.
+ * s_q       query tokens per sequence, 1 .. 64.
+ * heads     16, 32, 64 or 128.
+ * causal    0 or 1 (see the header comment); affects the visible key counts.
+ * num_workers  1 .. 4096; use mla_default_num_workers() for one run per compute unit.
+ * plan      device buffer of at least mla_plan_bytes(batch, s_q, heads, num_workers)
+ *           bytes, 16-byte aligned; written by the device. Opaque to the caller; valid
+ *           for every mla_decode_fwd call with the same seqlens contents, batch, s_q,
+ *           heads, causal and num_workers.
+ * Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL (plan_bytes),
+ * MLA_ERR_HIP. */
+int32_t mla_get_split_plan(const int32_t* seqlens, int32_t batch, int32_t s_q, int32_t heads,
+                           int32_t causal, int32_t num_workers, void* plan, size_t plan_bytes,
+                           void* stream);
+
+/* Latent-space MLA decode (the formulas in the header comment).
+ *
+ * q           device bf16 [batch, s_q, heads, 576], contiguous: absorbed queries
+ *             [q_nope W_k^T | q_rope] (rope rotation already applied).
+ * kv_cache    device, layout per kv_dtype (see mla_kv_dtype), 16-byte aligned.
+ * kv_scales   device float32 [num_pages, 64, 4] for MLA_KV_FP8_E4M3; must be NULL for bf16.
+ * kv_dtype    MLA_KV_BF16 or MLA_KV_FP8_E4M3.
+ * num_pages   pages in kv_cache (>= 1); page ids outside [0, num_pages) read as zeros.
+ * block_table device int32 [batch, max_pages], row-major.
+ * max_pages   1 .. 65535.
+ * seqlens     device int32 [batch] (same contents as given to the plan).
+ * batch, s_q, heads, causal   as for mla_get_split_plan (must match the plan).
+ * softmax_scale  multiplies every score (e.g. 1/sqrt(192)); finite and > 0.
+ * plan        device plan from mla_get_split_plan for the same arguments.
+ * num_workers the num_workers given to mla_get_split_plan.
+ * workspace   device buffer of at least mla_workspace_bytes(batch, s_q, heads,
+ *             num_workers) bytes, 16-byte aligned, or NULL when that size is 0. Scratch:
+ *             contents on entry are ignored, on return undefined.
+ * out         device float32 [batch, s_q, heads, 512] (normalised O_latent), 16-byte aligned.
+ * lse         device float32 [batch, s_q, heads] (natural-log log-sum-exp).
+ * Calls that overlap on the same workspace race. Results for a fixed plan are bitwise
+ * reproducible.
+ * Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP. */
+int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scales, int32_t kv_dtype,
+                       int64_t num_pages, const int32_t* block_table, int32_t max_pages,
+                       const int32_t* seqlens, int32_t batch, int32_t s_q, int32_t heads,
+                       float softmax_scale, int32_t causal, const void* plan, int32_t num_workers,
+                       void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMLA_H */

@@ -1,0 +1,166 @@
+"""mla_latent_space_amd: latent-space MLA decode on MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/libmla.h`` (``libmla.so`` in this
+package directory). The binding only marshals arguments: every step of the decode
+runs in the HIP kernels of the library; PyTorch provides device memory and streams.
+If ``libmla.so`` is missing, every call raises -- there is no fallback path.
+
+    plan = get_split_plan(seqlens, s_q, heads, causal=False)
+    out, lse = decode_fwd(q, kv_cache, block_table, seqlens, softmax_scale, plan=plan)
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["MlaError", "SplitPlan", "lib", "abi_version", "default_num_workers", "plan_bytes", "workspace_bytes",
+           "get_split_plan", "decode_fwd", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+_STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_WORKSPACE_TOO_SMALL",
+           4: "MLA_ERR_HIP", 5: "MLA_ERR_INTERNAL"}
+
+_lib = None
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m mla_latent_space_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    c_i32, c_i64, c_sz, c_p, c_f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    L.mla_abi_version.restype = c_i32
+    L.mla_abi_version.argtypes = []
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_status_string.argtypes = [c_i32]
+    L.mla_last_error_message.restype = ctypes.c_char_p
+    L.mla_last_error_message.argtypes = []
+    L.mla_default_num_workers.restype = c_i32
+    L.mla_default_num_workers.argtypes = [c_i32]
+    L.mla_plan_bytes.restype = c_sz
+    L.mla_plan_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32]
+    L.mla_workspace_bytes.restype = c_sz
+    L.mla_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32]
+    L.mla_get_split_plan.restype = c_i32
+    L.mla_get_split_plan.argtypes = [c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_p, c_sz, c_p]
+    L.mla_decode_fwd.restype = c_i32
+    L.mla_decode_fwd.argtypes = [c_p, c_p, c_p, c_i32, c_i64, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_f, c_i32,
+                                 c_p, c_i32, c_p, c_sz, c_p, c_p, c_p]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise MlaError(status, lib().mla_last_error_message().decode())
+
+
+def abi_version() -> int:
+    return int(lib().mla_abi_version())
+
+
+def default_num_workers(device: Optional[int] = None) -> int:
+    dev = torch.cuda.current_device() if device is None else int(device)
+    n = int(lib().mla_default_num_workers(dev))
+    if n < 0:
+        raise MlaError(4, lib().mla_last_error_message().decode())
+    return n
+
+
+def plan_bytes(batch: int, s_q: int, heads: int, num_workers: int) -> int:
+    return int(lib().mla_plan_bytes(batch, s_q, heads, num_workers))
+
+
+def workspace_bytes(batch: int, s_q: int, heads: int, num_workers: int) -> int:
+    return int(lib().mla_workspace_bytes(batch, s_q, heads, num_workers))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+@dataclasses.dataclass
+class SplitPlan:
+    """Device plan buffer plus the arguments it was built for."""
+    buffer: torch.Tensor
+    batch: int
+    s_q: int
+    heads: int
+    causal: bool
+    num_workers: int
+
+
+def get_split_plan(seqlens: torch.Tensor, s_q: int, heads: int, causal: bool = False,
+                   num_workers: Optional[int] = None) -> SplitPlan:
+    """Enqueue the split-KV planner on the current stream (see mla_get_split_plan)."""
+    if seqlens.dtype != torch.int32 or not seqlens.is_cuda or not seqlens.is_contiguous():
+        raise ValueError("seqlens must be a contiguous int32 CUDA tensor")
+    batch = seqlens.numel()
+    W = default_num_workers(seqlens.device.index) if num_workers is None else int(num_workers)
+    nbytes = plan_bytes(batch, s_q, heads, W)
+    if nbytes == 0:
+        _check(int(lib().mla_get_split_plan(None, batch, s_q, heads, int(causal), W, None, 0, None)))
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=seqlens.device)
+    _check(int(lib().mla_get_split_plan(seqlens.data_ptr(), batch, s_q, heads, int(causal), W, buf.data_ptr(),
+                                        nbytes, _stream(seqlens))))
+    return SplitPlan(buf, batch, s_q, heads, bool(causal), W)
+
+
+def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor,
+               softmax_scale: float, kv_scales: Optional[torch.Tensor] = None, causal: bool = False,
+               plan: Optional[SplitPlan] = None, workspace: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Latent-space MLA decode (see mla_decode_fwd). q: bf16 [b, s, h, 576]; kv_cache: bf16
+    [pages, 64, 576] or uint8 [pages, 64, 640] with kv_scales float32 [pages, 64, 4];
+    block_table int32 [b, max_pages]; seqlens int32 [b]. Returns out float32 [b, s, h, 512]
+    and lse float32 [b, s, h]."""
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, s_q, heads, 576]")
+    batch, s_q, heads, _ = q.shape
+    if kv_cache.dtype == torch.bfloat16:
+        kv_dtype = KV_BF16
+    elif kv_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        kv_dtype = KV_FP8_E4M3
+    else:
+        raise ValueError("kv_cache must be bfloat16, or uint8/float8_e4m3fn for the fp8 layout")
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table), ("seqlens", seqlens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if q.dtype != torch.bfloat16 or block_table.dtype != torch.int32 or seqlens.dtype != torch.int32:
+        raise ValueError("q must be bfloat16; block_table and seqlens int32")
+    if plan is None:
+        plan = get_split_plan(seqlens, s_q, heads, causal)
+    if (plan.batch, plan.s_q, plan.heads, plan.causal) != (batch, s_q, heads, bool(causal)):
+        raise ValueError("plan was built for different arguments")
+    W = plan.num_workers
+    need = workspace_bytes(batch, s_q, heads, W)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(batch, s_q, heads, 512, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(batch, s_q, heads, dtype=torch.float32, device=q.device)
+    status = lib().mla_decode_fwd(
+        q.data_ptr(), kv_cache.data_ptr(), None if kv_scales is None else kv_scales.data_ptr(), kv_dtype,
+        kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(), batch, s_q, heads,
+        float(softmax_scale), int(causal), plan.buffer.data_ptr(), W,
+        None if workspace is None else workspace.data_ptr(), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        out.data_ptr(), lse.data_ptr(), _stream(q))
+    _check(int(status))
+    return out, lse

@@ -1,0 +1,176 @@
+// libmla C ABI: host-side validation, sizing and dispatch. Every check here happens before
+// any work is enqueued; the library allocates nothing and keeps no pointer across calls.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/libmla.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int32_t ok() {
+  g_err[0] = '\0';
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by the plan and the decode call.
+int32_t check_shape(int32_t batch, int32_t s_q, int32_t heads, int32_t causal, int32_t num_workers) {
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (s_q < 1) return fail(MLA_ERR_INVALID_ARG, "s_q must be >= 1 (got %d)", s_q);
+  if (heads < 1) return fail(MLA_ERR_INVALID_ARG, "heads must be >= 1 (got %d)", heads);
+  if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (num_workers < 1) return fail(MLA_ERR_INVALID_ARG, "num_workers must be >= 1 (got %d)", num_workers);
+  if (s_q > 64) return fail(MLA_ERR_UNSUPPORTED, "s_q must be <= 64 (got %d)", s_q);
+  if (heads != 16 && heads != 32 && heads != 64 && heads != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "heads must be 16, 32, 64 or 128 (got %d)", heads);
+  if (batch > mla::kMaxItems) return fail(MLA_ERR_UNSUPPORTED, "batch must be <= %d (got %d)", mla::kMaxItems, batch);
+  const int64_t items = (int64_t)batch * mla::tiles_per_seq(s_q, heads);
+  if (items > mla::kMaxItems)
+    return fail(MLA_ERR_UNSUPPORTED, "batch * ceil(s_q*heads/128) must be <= %d (got %lld)", mla::kMaxItems,
+                (long long)items);
+  if (num_workers > mla::kMaxWorkers)
+    return fail(MLA_ERR_UNSUPPORTED, "num_workers must be <= %d (got %d)", mla::kMaxWorkers, num_workers);
+  return MLA_OK;
+}
+
+size_t plan_bytes_of(int32_t batch, int32_t s_q, int32_t heads, int32_t workers) {
+  const int n = batch * mla::tiles_per_seq(s_q, heads);
+  return (size_t)mla::plan_words(n, workers) * 4;
+}
+
+size_t workspace_bytes_of(int32_t batch, int32_t s_q, int32_t heads, int32_t workers) {
+  const int64_t n = (int64_t)batch * mla::tiles_per_seq(s_q, heads);
+  // split slots <= 2 * (active workers - 1); a split item needs >= 2 workers
+  int64_t slots = 2 * ((int64_t)workers - 1);
+  if (slots > 2 * n * workers) slots = 2 * n * workers;
+  if (slots < 0) slots = 0;
+  return (size_t)slots * (size_t)mla::kSlotFloats * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(int32_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    case MLA_ERR_INTERNAL: return "MLA_ERR_INTERNAL";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_last_error_message(void) { return g_err; }
+
+int32_t mla_default_num_workers(int32_t device) {
+  int count = 0;
+  hipError_t e = hipDeviceGetAttribute(&count, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) {
+    fail(MLA_ERR_HIP, "hipDeviceGetAttribute(MultiprocessorCount, %d): %s", device, hipGetErrorString(e));
+    return -1;
+  }
+  ok();
+  return count;
+}
+
+size_t mla_plan_bytes(int32_t batch, int32_t s_q, int32_t heads, int32_t num_workers) {
+  if (check_shape(batch, s_q, heads, 0, num_workers) != MLA_OK) return 0;
+  return plan_bytes_of(batch, s_q, heads, num_workers);
+}
+
+size_t mla_workspace_bytes(int32_t batch, int32_t s_q, int32_t heads, int32_t num_workers) {
+  if (check_shape(batch, s_q, heads, 0, num_workers) != MLA_OK) return 0;
+  return workspace_bytes_of(batch, s_q, heads, num_workers);
+}
+
+int32_t mla_get_split_plan(const int32_t* seqlens, int32_t batch, int32_t s_q, int32_t heads, int32_t causal,
+                           int32_t num_workers, void* plan, size_t plan_bytes, void* stream) {
+  int32_t st = check_shape(batch, s_q, heads, causal, num_workers);
+  if (st != MLA_OK) return st;
+  if (!seqlens) return fail(MLA_ERR_INVALID_ARG, "seqlens is NULL");
+  if (!plan) return fail(MLA_ERR_INVALID_ARG, "plan is NULL");
+  if (!aligned16(plan)) return fail(MLA_ERR_INVALID_ARG, "plan must be 16-byte aligned");
+  const size_t need = plan_bytes_of(batch, s_q, heads, num_workers);
+  if (plan_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "plan_bytes %zu < required %zu", plan_bytes, need);
+  hipError_t e = mla::launch_plan(seqlens, batch, s_q, heads, causal, num_workers, static_cast<int32_t*>(plan),
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scales, int32_t kv_dtype,
+                       int64_t num_pages, const int32_t* block_table, int32_t max_pages, const int32_t* seqlens,
+                       int32_t batch, int32_t s_q, int32_t heads, float softmax_scale, int32_t causal,
+                       const void* plan, int32_t num_workers, void* workspace, size_t workspace_bytes, float* out,
+                       float* lse, void* stream) {
+  int32_t st = check_shape(batch, s_q, heads, causal, num_workers);
+  if (st != MLA_OK) return st;
+  if (!q || !kv_cache || !block_table || !seqlens || !plan || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL (q, kv_cache, block_table, seqlens, plan, out, lse)");
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_INVALID_ARG, "kv_dtype must be MLA_KV_BF16 or MLA_KV_FP8_E4M3 (got %d)", kv_dtype);
+  if (kv_dtype == MLA_KV_FP8_E4M3 && !kv_scales)
+    return fail(MLA_ERR_INVALID_ARG, "kv_scales is required for an fp8 cache");
+  if (kv_dtype == MLA_KV_BF16 && kv_scales)
+    return fail(MLA_ERR_INVALID_ARG, "kv_scales must be NULL for a bf16 cache");
+  if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1 (got %lld)", (long long)num_pages);
+  if (max_pages < 1 || max_pages > mla::kMaxPagesPerSeq)
+    return fail(max_pages < 1 ? MLA_ERR_INVALID_ARG : MLA_ERR_UNSUPPORTED, "max_pages must be in 1..%d (got %d)",
+                mla::kMaxPagesPerSeq, max_pages);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) || !aligned16(plan) ||
+      (kv_scales && !aligned16(kv_scales)) || (workspace && !aligned16(workspace)))
+    return fail(MLA_ERR_INVALID_ARG, "q, kv_cache, kv_scales, out, plan and workspace must be 16-byte aligned");
+  const size_t need = workspace_bytes_of(batch, s_q, heads, num_workers);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace ? workspace_bytes : 0,
+                need);
+  mla::DecodeArgs a;
+  a.q = q;
+  a.kv = kv_cache;
+  a.kv_scales = kv_scales;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.seqlens = seqlens;
+  a.batch = batch;
+  a.s_q = s_q;
+  a.heads = heads;
+  a.causal = causal;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.plan = static_cast<const int32_t*>(plan);
+  a.workers = num_workers;
+  a.ws = static_cast<float*>(workspace);
+  a.out = out;
+  a.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = kv_dtype == MLA_KV_BF16 ? mla::launch_decode_bf16(a, s) : mla::launch_decode_fp8(a, s);
+  if (e == hipErrorNotSupported) return fail(MLA_ERR_UNSUPPORTED, "this cache dtype is not built in this library");
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
+  e = mla::launch_combine(a, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

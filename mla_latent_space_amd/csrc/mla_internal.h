@@ -1,0 +1,74 @@
+// Internal constants and device-plan layout shared by the libmla host code and kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kPage = 64;          // tokens per cache page
+constexpr int kLat = 512;          // latent (c_KV) channels, the value width
+constexpr int kRope = 64;          // shared rope key channels
+constexpr int kDqk = kLat + kRope; // 576: absorbed query / cached row width
+constexpr int kRowsPerTile = 128;  // query rows (token, head) per work item
+constexpr int kFp8RowBytes = kLat + 2 * kRope;  // 640
+constexpr int kFp8Tiles = kLat / 128;           // 4 scales per token
+
+// Planner limits.
+constexpr int kMaxItems = 16384;
+constexpr int kMaxWorkers = 4096;
+constexpr int kMaxPagesPerSeq = 65535;
+constexpr int kPlanOverhead = 2;   // per-item cost in page units (queries in, rows out)
+
+// Plan buffer (int32 words).
+constexpr int kPlanMagic = 0x4D4C4150;  // 'MLAP'
+enum PlanHeader {
+  kHMagic = 0, kHVersion, kHBatch, kHSq, kHHeads, kHCausal, kHWorkers, kHTiles, kHItems,
+  kHOverhead, kHTotalCost, kHActiveWorkers, kHSplitItems, kHSlots, kHReserved0, kHReserved1,
+  kHeaderWords = 16
+};
+// item record (sorted order): seq, tile, vis, pages, cost_begin, owner, nsplits, slot_base
+constexpr int kItemWords = 8;
+enum ItemField { kISeq = 0, kITile, kIVis, kIPages, kICost, kIOwner, kINsplits, kISlot };
+// worker record: item_begin, page_begin, item_end, page_end (end exclusive)
+constexpr int kWorkerWords = 4;
+
+__host__ __device__ inline int plan_items_off() { return kHeaderWords; }
+__host__ __device__ inline int plan_workers_off(int n_items) { return kHeaderWords + kItemWords * n_items; }
+__host__ __device__ inline int plan_split_off(int n_items, int workers) {
+  return plan_workers_off(n_items) + kWorkerWords * workers;
+}
+__host__ __device__ inline int64_t plan_words(int n_items, int workers) {
+  return (int64_t)plan_split_off(n_items, workers) + n_items;
+}
+__host__ __device__ inline int tiles_per_seq(int s_q, int heads) {
+  return (s_q * heads + kRowsPerTile - 1) / kRowsPerTile;
+}
+
+// Workspace: per partial slot, 128 rows x 512 fp32 (normalised partial out) + 128 fp32 lse.
+constexpr int64_t kSlotFloats = (int64_t)kRowsPerTile * kLat + kRowsPerTile;
+
+hipError_t launch_plan(const int32_t* seqlens, int batch, int s_q, int heads, int causal, int workers,
+                       int32_t* plan, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* kv;
+  const float* kv_scales;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int max_pages;
+  const int32_t* seqlens;
+  int batch, s_q, heads, causal;
+  float scale_log2;   // softmax_scale * log2(e)
+  const int32_t* plan;
+  int workers;
+  float* ws;          // partial slots
+  float* out;
+  float* lse;
+};
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace mla

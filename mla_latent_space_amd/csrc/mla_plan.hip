@@ -1,0 +1,240 @@
+// Split-KV planner: one 1024-thread work-group builds the whole plan on the device.
+//
+// FlashMLA-2 newsletter page, section "Architectural Analysis": a radix-sorted block
+// scheduler balances sequence partitions across compute units so that 128-token and
+// 128k-token sequences in one batch leave no stragglers. This kernel is that idea on
+// gfx950: items (sequence, 128-row tile) are keyed by page count, sorted longest first
+// by a two-pass LSD radix sort in LDS (8-bit digits, wave ballots for the stable rank),
+// costed as overhead + pages, prefix-summed, and cut into equal-cost contiguous runs,
+// one per worker (one persistent decode work-group per compute unit).
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__device__ inline void item_shape(const int32_t* seqlens, int idx, int tiles, int s_q, int heads, int causal,
+                                  int* seq, int* tile, int* vis, int* pages) {
+  const int sq = idx / tiles, tl = idx - sq * tiles;
+  int t = seqlens[sq];
+  t = t < 0 ? 0 : t;
+  const int cap = kMaxPagesPerSeq * kPage;
+  t = t > cap ? cap : t;
+  int v = t;
+  if (causal) {
+    const int rows = s_q * heads;
+    int last_row = (tl + 1) * kRowsPerTile;
+    last_row = (last_row < rows ? last_row : rows) - 1;
+    const int j_last = last_row / heads;
+    v = t - s_q + 1 + j_last;
+    v = v < 0 ? 0 : (v > t ? t : v);
+  }
+  int p = (v + kPage - 1) / kPage;
+  *seq = sq; *tile = tl; *vis = v; *pages = p < 1 ? 1 : p;
+}
+
+// Exclusive scan over the block: each thread contributes `x`, returns its exclusive prefix,
+// `total` gets the block sum. `scratch` holds >= kWaves ints.
+__device__ inline int block_exclusive_scan(int x, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int wave_off = 0, tot = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const int s = scratch[w];
+    wave_off += (w < wave) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return wave_off + incl - x;
+}
+
+__device__ inline int worker_of(int64_t x, int64_t total, int64_t W) {
+  return (int)(((x + 1) * W - 1) / total);
+}
+
+__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restrict__ seqlens, int batch, int s_q,
+                                                         int heads, int causal, int W, int32_t* __restrict__ plan) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t sm[];
+  uint32_t* keys_a = sm;
+  uint32_t* keys_b = sm + kMaxItems;
+  int* wave_cnt = reinterpret_cast<int*>(keys_b + kMaxItems);   // [kWaves][256]
+  int* digit_base = wave_cnt + kWaves * 256;                    // [256]
+  int* tile_tot = digit_base + 256;                             // [256]
+  int* scratch = tile_tot + 256;                                // [kWaves]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tiles = tiles_per_seq(s_q, heads);
+  const int n = batch * tiles;
+
+  // keys: (0xFFFF - pages) in the high half sorts longest first; the item index in the
+  // low half is already ascending, and the LSD passes are stable.
+  for (int i = tid; i < n; i += kThreads) {
+    int sq, tl, vis, pages;
+    item_shape(seqlens, i, tiles, s_q, heads, causal, &sq, &tl, &vis, &pages);
+    keys_a[i] = ((uint32_t)(0xFFFF - pages) << 16) | (uint32_t)i;
+  }
+  __syncthreads();
+
+  uint32_t* src = keys_a;
+  uint32_t* dst = keys_b;
+  for (int shift = 16; shift < 32; shift += 8) {
+    if (tid < 256) digit_base[tid] = 0;
+    for (int i = tid; i < kWaves * 256; i += kThreads) wave_cnt[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kThreads) atomicAdd(&digit_base[(src[i] >> shift) & 255], 1);
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int d = 0; d < 256; ++d) { const int c = digit_base[d]; digit_base[d] = run; run += c; }
+    }
+    __syncthreads();
+    for (int t0 = 0; t0 < n; t0 += kThreads) {
+      const int i = t0 + tid;
+      const bool valid = i < n;
+      const uint32_t v = valid ? src[i] : 0u;
+      const int d = (int)((v >> shift) & 255);
+      uint64_t peers = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint64_t bb = __ballot((d >> b) & 1);
+        peers &= ((d >> b) & 1) ? bb : ~bb;
+      }
+      const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+      if (valid && rank == 0) wave_cnt[wave * 256 + d] = __popcll(peers);
+      __syncthreads();
+      if (tid < 256) {
+        int run = 0;
+        for (int w = 0; w < kWaves; ++w) {
+          const int c = wave_cnt[w * 256 + tid];
+          wave_cnt[w * 256 + tid] = run;
+          run += c;
+        }
+        tile_tot[tid] = run;
+      }
+      __syncthreads();
+      if (valid) dst[digit_base[d] + wave_cnt[wave * 256 + d] + rank] = v;
+      __syncthreads();
+      if (tid < 256) {
+        digit_base[tid] += tile_tot[tid];
+        for (int w = 0; w < kWaves; ++w) wave_cnt[w * 256 + tid] = 0;
+      }
+      __syncthreads();
+    }
+    uint32_t* tmp = src; src = dst; dst = tmp;
+  }
+  // src holds the sorted keys; dst becomes the cost prefix C_k.
+  int* cost = reinterpret_cast<int*>(dst);
+  const int per = (n + kThreads - 1) / kThreads;
+  const int lo = tid * per;
+  const int hi = lo + per < n ? lo + per : n;
+  int local = 0;
+  for (int k = lo; k < hi; ++k) local += kPlanOverhead + (0xFFFF - (int)(src[k] >> 16));
+  int total = 0;
+  int run = block_exclusive_scan(local, scratch, &total);
+  for (int k = lo; k < hi; ++k) {
+    cost[k] = run;
+    run += kPlanOverhead + (0xFFFF - (int)(src[k] >> 16));
+  }
+  __syncthreads();
+  const int64_t C = total;
+  const int64_t Weff = (int64_t)W < C ? (int64_t)W : C;
+
+  // owners, splits; slots and split-list positions by one packed scan
+  int local_pack = 0;
+  for (int k = lo; k < hi; ++k) {
+    const int pages = 0xFFFF - (int)(src[k] >> 16);
+    const int first = worker_of((int64_t)cost[k] + kPlanOverhead, C, Weff);
+    const int last = worker_of((int64_t)cost[k] + kPlanOverhead + pages - 1, C, Weff);
+    const int ns = last - first + 1;
+    local_pack += ns > 1 ? ((ns << 16) | 1) : 0;
+  }
+  int pack_total = 0;
+  int pack_run = block_exclusive_scan(local_pack, scratch, &pack_total);
+  int32_t* items = plan + plan_items_off();
+  int32_t* split_list = plan + plan_split_off(n, W);
+  for (int k = lo; k < hi; ++k) {
+    const uint32_t key = src[k];
+    const int idx = (int)(key & 0xFFFF);
+    int sq, tl, vis, pages;
+    item_shape(seqlens, idx, tiles, s_q, heads, causal, &sq, &tl, &vis, &pages);
+    const int first = worker_of((int64_t)cost[k] + kPlanOverhead, C, Weff);
+    const int last = worker_of((int64_t)cost[k] + kPlanOverhead + pages - 1, C, Weff);
+    const int ns = last - first + 1;
+    int32_t* it = items + kItemWords * k;
+    it[kISeq] = sq;
+    it[kITile] = tl;
+    it[kIVis] = vis;
+    it[kIPages] = pages;
+    it[kICost] = cost[k];
+    it[kIOwner] = first;
+    it[kINsplits] = ns;
+    it[kISlot] = ns > 1 ? (pack_run >> 16) : -1;
+    if (ns > 1) split_list[pack_run & 0xFFFF] = k;
+    pack_run += ns > 1 ? ((ns << 16) | 1) : 0;
+  }
+  // workers: start(w) = (item holding position floor(w C / Weff), page offset)
+  int32_t* workers = plan + plan_workers_off(n);
+  for (int w = tid; w < W; w += kThreads) {
+    int sk[2], sp[2];
+    for (int e = 0; e < 2; ++e) {
+      const int64_t ww = w + e;
+      if (ww >= Weff) { sk[e] = n; sp[e] = 0; continue; }
+      const int64_t b = (ww * C) / Weff;
+      int l = 0, r = n - 1;   // largest k with cost[k] <= b
+      while (l < r) {
+        const int m = (l + r + 1) >> 1;
+        if ((int64_t)cost[m] <= b) l = m; else r = m - 1;
+      }
+      sk[e] = l;
+      const int64_t off = b - cost[l] - kPlanOverhead;
+      sp[e] = off > 0 ? (int)off : 0;
+    }
+    int32_t* wr = workers + kWorkerWords * w;
+    wr[0] = sk[0]; wr[1] = sp[0]; wr[2] = sk[1]; wr[3] = sp[1];
+  }
+  if (tid == 0) {
+    plan[kHMagic] = kPlanMagic;
+    plan[kHVersion] = 1;
+    plan[kHBatch] = batch;
+    plan[kHSq] = s_q;
+    plan[kHHeads] = heads;
+    plan[kHCausal] = causal;
+    plan[kHWorkers] = W;
+    plan[kHTiles] = tiles;
+    plan[kHItems] = n;
+    plan[kHOverhead] = kPlanOverhead;
+    plan[kHTotalCost] = total;
+    plan[kHActiveWorkers] = (int)Weff;
+    plan[kHSplitItems] = pack_total & 0xFFFF;
+    plan[kHSlots] = pack_total >> 16;
+    plan[kHReserved0] = 0;
+    plan[kHReserved1] = 0;
+  }
+}
+
+constexpr size_t kPlanLds = (size_t)2 * kMaxItems * 4 + (size_t)(kWaves * 256 + 256 + 256 + kWaves) * 4;
+
+}  // namespace
+
+hipError_t launch_plan(const int32_t* seqlens, int batch, int s_q, int heads, int causal, int workers,
+                       int32_t* plan, hipStream_t stream) {
+  static_assert(kPlanLds <= 160 * 1024, "plan LDS");
+  hipError_t e = hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)kPlanLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), kPlanLds, stream, seqlens, batch, s_q, heads, causal,
+                     workers, plan);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,56 @@
+"""Helpers shared by the GPU tests: upload a workload, run the library, compare with the oracle."""
+import numpy as np
+import torch
+
+import mla_latent_space_amd as mla
+
+# Tolerances on out (float32 [b, s, h, 512]) and lse. bf16 cache: rel L2 <= 5e-3, max abs
+# <= 2e-2, |d lse| <= 1e-3. fp8 cache: compared with the oracle on the same dequantised
+# values, rel L2 <= 3e-2; every e4m3 code is exact in bf16 and the scales are applied in
+# fp32, so the remaining error sources are those of the bf16 path and its max abs / lse
+# bounds are kept.
+BF16_TOL = dict(rel_l2=5e-3, max_abs=2e-2, lse=1e-3)
+FP8_TOL = dict(rel_l2=3e-2, max_abs=2e-2, lse=1e-3)
+
+
+class Dev:
+    """A workload's arrays on the GPU."""
+
+    def __init__(self, w, device="cuda"):
+        self.w = w
+        self.q = torch.from_numpy(w.q.view(np.int16)).to(device).view(torch.bfloat16)
+        if w.kv_dtype == "bf16":
+            self.kv = torch.from_numpy(w.kv.view(np.int16)).to(device).view(torch.bfloat16)
+            self.scales = None
+        else:
+            self.kv = torch.from_numpy(w.kv).to(device)
+            self.scales = torch.from_numpy(w.kv_scales).to(device)
+        self.bt = torch.from_numpy(w.block_table).to(device)
+        self.sl = torch.from_numpy(w.seqlens).to(device)
+
+    def plan(self, num_workers=None):
+        return mla.get_split_plan(self.sl, self.w.s_q, self.w.heads, self.w.causal, num_workers)
+
+    def run(self, num_workers=None, plan=None):
+        if plan is None:
+            plan = self.plan(num_workers)
+        out, lse = mla.decode_fwd(self.q, self.kv, self.bt, self.sl, self.w.scale, kv_scales=self.scales,
+                                  causal=self.w.causal, plan=plan)
+        torch.cuda.synchronize()
+        return out, lse
+
+
+def compare(out, lse, ref_out, ref_lse, tol, what=""):
+    """Relative L2 and max abs over out, max |d lse| over finite lse; -inf must match."""
+    out = np.asarray(out, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    assert np.isfinite(out).all(), f"{what}: non-finite out"
+    ninf = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), ninf), f"{what}: -inf lse pattern differs"
+    denom = np.linalg.norm(ref_out)
+    rel = np.linalg.norm(out - ref_out) / (denom if denom > 0 else 1.0)
+    mabs = float(np.max(np.abs(out - ref_out))) if out.size else 0.0
+    dl = float(np.max(np.abs(lse[~ninf] - ref_lse[~ninf]))) if (~ninf).any() else 0.0
+    msg = f"{what}: rel_l2={rel:.3e} max_abs={mabs:.3e} max_dlse={dl:.3e}"
+    assert rel <= tol["rel_l2"] and mabs <= tol["max_abs"] and dl <= tol["lse"], msg
+    return rel, mabs, dl

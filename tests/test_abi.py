@@ -1,0 +1,98 @@
+"""The C ABI library loads, exports every declared entry point, and rejects bad arguments on
+the host before any HIP call (CPU only: no compute is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_space_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmla.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mla.LIB_PATH), reason="libmla.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"mla_get_split_plan", "mla_decode_fwd", "mla_plan_bytes", "mla_workspace_bytes"} <= set(names)
+    L = ctypes.CDLL(mla.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = mla.lib()
+    assert mla.abi_version() == 1
+    assert L.mla_status_string(0) == b"MLA_OK"
+    assert L.mla_status_string(3) == b"MLA_ERR_WORKSPACE_TOO_SMALL"
+    assert L.mla_status_string(99) == b"unknown status"
+
+
+def test_sizes():
+    # 64 items (one 128-row tile each), 256 workers
+    n, W = 64, 256
+    assert mla.plan_bytes(64, 1, 128, W) == 4 * (16 + 8 * n + 4 * W + n)
+    assert mla.plan_bytes(32, 16, 128, W) == 4 * (16 + 9 * 32 * 16 + 4 * W)
+    assert mla.workspace_bytes(64, 1, 128, W) == 2 * (W - 1) * (128 * 512 + 128) * 4
+    assert mla.workspace_bytes(64, 1, 128, 1) == 0
+    for bad in [(0, 1, 128, W), (4, 0, 128, W), (4, 1, 96, W), (4, 65, 128, W), (4, 1, 128, 0), (4, 1, 128, 5000),
+                (20000, 1, 128, W), (2000, 16, 128, W)]:
+        assert mla.plan_bytes(*bad) == 0, bad
+        assert mla.workspace_bytes(*bad) == 0, bad
+
+
+def _plan(L, seqlens, batch, s_q, h, causal, W, plan, nbytes):
+    return L.mla_get_split_plan(seqlens, batch, s_q, h, causal, W, plan, nbytes, None)
+
+
+def test_plan_rejects_bad_arguments_before_launch():
+    L = mla.lib()
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: every case fails validation first
+    need = mla.plan_bytes(4, 1, 128, 8)
+    assert _plan(L, None, 4, 1, 128, 0, 8, fake, need) == 1
+    assert _plan(L, fake, 4, 1, 128, 0, 8, None, need) == 1
+    assert _plan(L, fake, 4, 1, 128, 2, 8, fake, need) == 1
+    assert _plan(L, fake, 4, 1, 100, 0, 8, fake, need) == 2
+    assert _plan(L, fake, 4, 1, 128, 0, 8, fake, need - 4) == 3
+    assert b"plan_bytes" in L.mla_last_error_message()
+    assert _plan(L, fake, 4, 1, 128, 0, 8, ctypes.c_void_p(0x100004), need) == 1   # misaligned
+
+
+def _decode(L, **kw):
+    fake = ctypes.c_void_p(0x100000)
+    a = dict(q=fake, kv=fake, scales=None, dtype=0, num_pages=10, bt=fake, max_pages=4, sl=fake, batch=2, s_q=1,
+             h=128, scale=0.07, causal=0, plan=fake, W=8, ws=fake, ws_bytes=1 << 30, out=fake, lse=fake)
+    a.update(kw)
+    return L.mla_decode_fwd(a["q"], a["kv"], a["scales"], a["dtype"], a["num_pages"], a["bt"], a["max_pages"], a["sl"],
+                            a["batch"], a["s_q"], a["h"], a["scale"], a["causal"], a["plan"], a["W"], a["ws"],
+                            a["ws_bytes"], a["out"], a["lse"], None)
+
+
+def test_decode_rejects_bad_arguments_before_launch():
+    L = mla.lib()
+    fake = ctypes.c_void_p(0x100000)
+    assert _decode(L, q=None) == 1
+    assert _decode(L, lse=None) == 1
+    assert _decode(L, dtype=7) == 1
+    assert _decode(L, dtype=1) == 1                      # fp8 without scales
+    assert _decode(L, scales=fake) == 1                  # bf16 with scales
+    assert _decode(L, num_pages=0) == 1
+    assert _decode(L, max_pages=0) == 1
+    assert _decode(L, max_pages=70000) == 2
+    assert _decode(L, scale=0.0) == 1
+    assert _decode(L, scale=float("nan")) == 1
+    assert _decode(L, h=48) == 2
+    assert _decode(L, s_q=65) == 2
+    assert _decode(L, causal=3) == 1
+    assert _decode(L, ws_bytes=16) == 3
+    assert _decode(L, ws=None) == 3
+    assert _decode(L, out=ctypes.c_void_p(0x100008)) == 1  # misaligned
+    assert b"16-byte aligned" in L.mla_last_error_message()
