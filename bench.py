@@ -1,0 +1,218 @@
+"""Benchmark: latent-space MLA decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3|jagged|spec|fp8|tiny]
+
+One step = the whole hot path over one batch: the split plan (mla_get_split_plan) and the
+decode with its split combine (mla_decode_fwd), with inputs already resident in HBM. The
+default workload is the DeepSeek-V3-shaped decode b=64, s=1, h=128, t=4096, k=512, p=64,
+bf16 paged cache (64-token pages in shuffled physical order), fp32 out + lse.
+
+To keep the 256 MB Infinity Cache from serving the KV cache, the step cycles through
+`--rotate` full copies of the cache (>= 1 GiB in total by default).
+
+Prints ONE JSON line (metric, value = us per step, roofline of the decode call, cpu_baseline
+= the fp64 oracle timed on a bounded sample of the same workload on the host cores).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode µs/call, TFLOPS + HBM GB/s (% roofline), b=64 h=128 t=4096 bf16"
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+K_LAT, P_ROPE = 512, 64
+
+
+def workload_bytes(w) -> float:
+    """Algorithmic HBM bytes of one decode call at the real dtypes: the live tokens of the
+    cache, the queries, out (fp32) and lse (fp32), block table and lengths."""
+    import numpy as np
+    per_tok = 576 * 2 if w.kv_dtype == "bf16" else 640 + 16
+    kv = float(np.sum(w.seqlens.astype(np.int64))) * per_tok
+    return kv + w.q.size * 2 + w.batch * w.s_q * w.heads * (K_LAT * 4 + 4) + w.block_table.size * 4 + w.batch * 4
+
+
+def workload_flops(w) -> float:
+    """2*b*h*s*t*(2k+p) (the page's FlashMLA cost model), summed over sequences."""
+    return float(sum(2.0 * w.heads * w.s_q * int(t) * (2 * K_LAT + P_ROPE) for t in w.seqlens))
+
+
+def describe(w) -> str:
+    import numpy as np
+    lens = w.seqlens
+    t = f"t={int(lens[0])}" if np.all(lens == lens[0]) else f"t={int(lens.min())}..{int(lens.max())} (sum {int(lens.sum())})"
+    return (f"{w.name}: b={w.batch} s={w.s_q} h={w.heads} k=512 p=64 {t} {w.kv_dtype} cache, 64-token pages "
+            f"in shuffled order{', causal' if w.causal else ''}, fp32 out+lse")
+
+
+def traffic_from_profile(kernel_srcs, key):
+    """HBM traffic of the decode call from a committed rocprofv3 PMC summary, only if it was
+    taken on the current kernel sources (sha256 of the .hip files)."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    h = hashlib.sha256()
+    for p in kernel_srcs:
+        h.update(open(p, "rb").read())
+    if rec.get("sources_sha256") != h.hexdigest():
+        return None
+    return rec.get(key, {}).get("bytes_per_call")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle (as is) on the first sequences of the workload until ~budget_s of host time,
+    extrapolated to the whole batch."""
+    import numpy as np
+    from oracle import mla as om
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.batch and (time.perf_counter() - t0) < budget_s:
+        om.decode_latent(w.q, w.kv, w.kv_scales, w.kv_dtype, w.block_table, w.seqlens, w.scale, w.causal, [done])
+        done += 1
+    el = time.perf_counter() - t0
+    frac = float(np.sum(w.seqlens[:done].astype(np.int64))) / float(np.sum(w.seqlens.astype(np.int64)))
+    us = el / frac * 1e6
+    return {"value": round(us, 1), "unit": "µs/call", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle on {done} of {w.batch} sequences ({frac * 100:.1f}% of the tokens) of the "
+                      f"{w.name} workload, {el:.1f} s, scaled to the whole batch"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--rotate", type=int, default=0, help="KV copies to cycle through (0: enough for >= 1 GiB)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build measures the single-GPU decode path "
+              "(see the sharding notes in DESIGN.md); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mla_latent_space_amd as mla
+    from mla_latent_space_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    w = wl.make_config(args.workload)
+    dev = torch.device("cuda", 0)
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    if w.kv_dtype == "bf16":
+        kv0 = torch.from_numpy(w.kv.view(np.int16)).to(dev).view(torch.bfloat16)
+        sc0 = None
+    else:
+        kv0 = torch.from_numpy(w.kv).to(dev)
+        sc0 = torch.from_numpy(w.kv_scales).to(dev)
+    kv_bytes = kv0.numel() * kv0.element_size() + (0 if sc0 is None else sc0.numel() * 4)
+    rot = args.rotate or max(1, math.ceil((1 << 30) / kv_bytes))
+    kvs = [kv0] + [kv0.clone() for _ in range(rot - 1)]
+    scs = [sc0] + [None if sc0 is None else sc0.clone() for _ in range(rot - 1)]
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seqlens).to(dev)
+    W = mla.default_num_workers(0)
+    out = torch.empty(w.batch, w.s_q, w.heads, 512, dtype=torch.float32, device=dev)
+    lse = torch.empty(w.batch, w.s_q, w.heads, dtype=torch.float32, device=dev)
+    ws_bytes = mla.workspace_bytes(w.batch, w.s_q, w.heads, W)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    plan_holder = {}
+
+    def step(i):
+        plan = mla.get_split_plan(sl, w.s_q, w.heads, w.causal, W)
+        plan_holder["p"] = plan
+        mla.decode_fwd(q, kvs[i % rot], bt, sl, w.scale, kv_scales=scs[i % rot], causal=w.causal, plan=plan,
+                       workspace=ws, out=out, lse=lse)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    # per-call events on the launch stream: plan, decode (decode kernel + split combine)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        a, b, c = ev[i]
+        a.record(stream)
+        plan = mla.get_split_plan(sl, w.s_q, w.heads, w.causal, W)
+        b.record(stream)
+        mla.decode_fwd(q, kvs[i % rot], bt, sl, w.scale, kv_scales=scs[i % rot], causal=w.causal, plan=plan,
+                       workspace=ws, out=out, lse=lse)
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    plan_us = np.array([ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(args.steps)])
+    dec_us = np.array([ev[i][1].elapsed_time(ev[i][2]) * 1e3 for i in range(args.steps)])
+    step_us = wall / args.steps * 1e6
+
+    flops = workload_flops(w)
+    byts = workload_bytes(w)
+    dec_mean = float(dec_us.mean())
+    achieved_gbps = byts / (dec_mean * 1e-6) / 1e9
+    tflops = flops / (dec_mean * 1e-6) / 1e12
+    ai = flops / byts
+    bound_us = max(byts / (PEAK_HBM_GBPS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
+    bound = "hbm" if byts / (PEAK_HBM_GBPS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12) else "mfma"
+    srcs = [os.path.join(ROOT, "mla_latent_space_amd", "csrc", f) for f in ("mla_decode.hip", "mla_plan.hip")]
+    traffic = traffic_from_profile(srcs, args.workload)
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    rec = {
+        "metric": METRIC,
+        "value": round(step_us, 2),
+        "unit": "µs/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": describe(w), "kv_copies_rotated": rot, "num_workers": W},
+        "decode_us": round(dec_mean, 2),
+        "decode_us_p10_p50_p90": [round(float(np.percentile(dec_us, p)), 2) for p in (10, 50, 90)],
+        "plan_us": round(float(plan_us.mean()), 2),
+        "tflops": round(tflops, 1),
+        "hbm_gbps": round(achieved_gbps, 1),
+        "arith_intensity": round(ai, 1),
+        "roofline_bound_us": round(bound_us, 2),
+        "roofline_frac_of_bound": round(bound_us / dec_mean, 4),
+        "roofline": dict(roof, kernel="mla_decode_fwd: decode kernel + split combine",
+                         bytes_per_call=byts, flops_per_call=flops),
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,7 +5,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/libmla.h"
+#include "libmla.h"
 #include "mla_internal.h"
 
 namespace {

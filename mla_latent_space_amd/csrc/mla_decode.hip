@@ -102,7 +102,7 @@ __device__ __forceinline__ void lds_dma_x4(uint32_t lds_addr, uint32_t voff, i32
       "buffer_load_dwordx4 %1, %2, 0 offen lds"
       :
       : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
-      : "memory", "m0");
+      : "m0");
 }
 
 // Work-group barrier for LDS traffic only. __syncthreads() also orders the LDS-DMA loads
@@ -132,53 +132,84 @@ __device__ __forceinline__ Seg seg_of(const int32_t* plan, int k, int kb, int pb
   return s;
 }
 
-// Load cursor: walks the worker's steps in order, kNBuf-1 steps ahead of the compute loop.
+// Load cursor: walks the worker's steps in order, ahead of the compute loop. The fields of
+// the current item are cached and the page id of the cursor's step is fetched when the
+// cursor moves, one compute region before its descriptor is needed, so the scalar load's
+// latency is covered by the barriers in between.
 struct LoadCursor {
   int k, hh, hh1;   // current item, next step to load, end step of that item
+  int seq, vis;     // fields of item k
+  int pid;          // page id of step hh (-1: none)
 };
 
-template <bool kFp8>
-struct Loader;
+__device__ __forceinline__ void cursor_fetch(LoadCursor& c, const Scalars& a, const int32_t* __restrict__ block_table) {
+  const int pg = c.hh >> 1;
+  c.pid = pg < a.max_pages ? block_table[(int64_t)c.seq * a.max_pages + pg] : -1;
+}
 
-template <>
-struct Loader<false> {
-  // Issue this wave's share of the 36 LDS-DMA loads of step (item k, half hh) into a ring slot.
-  __device__ __forceinline__ static void issue(const Scalars& a, const char* __restrict__ kv,
-                                               const int32_t* __restrict__ block_table,
-                                               const int32_t* __restrict__ plan, int k, int hh,
-                                               char __attribute__((address_space(3)))* lds_slot, int lane,
-                                               int wave) {
-    const int32_t* it = plan + plan_items_off() + kItemWords * k;
-    const int seq = it[kISeq], vis = it[kIVis];
-    const int pg = hh >> 1;
-    int pid = -1;
-    if (pg < a.max_pages) pid = block_table[(int64_t)seq * a.max_pages + pg];
-    int valid = vis - kStep * hh;
-    valid = valid > kStep ? kStep : valid;
-    const bool ok = pid >= 0 && (int64_t)pid < a.num_pages && valid > 0;
-    const char* base = kv +
-                       (ok ? ((int64_t)pid * (kPage * kRowBytes) + (int64_t)(hh & 1) * kBufBytes) : 0);
-    const uint64_t addr = reinterpret_cast<uint64_t>(base);
-    i32x4 rsrc;
-    rsrc[0] = (int)(uint32_t)addr;
-    rsrc[1] = (int)((uint32_t)(addr >> 32) & 0xFFFF);   // stride 0
-    rsrc[2] = ok ? valid * kRowBytes : 0;               // num_records: bytes past it read as 0
-    rsrc[3] = (int)kRsrcWord3;
-    const uint32_t lds_base = (uint32_t)(uintptr_t)lds_slot;
-    // Instruction i (1 KiB, 64 lanes x 16 B, lane-linear in LDS) is issued by wave i % 8.
-    // LDS chunk position p = 72u + pc holds logical chunk ch = pc ^ swz(u) of token u.
+__device__ __forceinline__ void cursor_enter(LoadCursor& c, const int32_t* __restrict__ plan, int k, int kb, int pb,
+                                             int ke, int pe) {
+  const int32_t* it = plan + plan_items_off() + kItemWords * k;
+  const Seg sg = seg_of(plan, k, kb, pb, ke, pe);
+  c.k = k;
+  c.seq = it[kISeq];
+  c.vis = it[kIVis];
+  c.hh = sg.hh0;
+  c.hh1 = sg.hh1;
+}
+
+// Buffer descriptor of the cursor's step (32 tokens = half of a 64-token page): base at the
+// step's first row, record count at the last visible token, so rows past it read as zeros.
+// A page id outside [0, num_pages) gives 0 records (all zeros).
+__device__ __forceinline__ i32x4 cursor_rsrc(const LoadCursor& c, const Scalars& a, const char* __restrict__ kv) {
+  int valid = c.vis - kStep * c.hh;
+  valid = valid > kStep ? kStep : valid;
+  const bool ok = c.pid >= 0 && (int64_t)c.pid < a.num_pages && valid > 0;
+  const uint64_t addr = reinterpret_cast<uint64_t>(kv) +
+                        (ok ? ((uint64_t)c.pid * (kPage * kRowBytes) + (uint64_t)(c.hh & 1) * kBufBytes) : 0);
+  // (uniform by construction; readfirstlane tells the compiler so, keeping it in SGPRs)
+  i32x4 rsrc;
+  rsrc[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+  rsrc[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(addr >> 32) & 0xFFFF));   // stride 0
+  rsrc[2] = __builtin_amdgcn_readfirstlane(ok ? valid * kRowBytes : 0);              // num_records
+  rsrc[3] = (int)kRsrcWord3;
+  return rsrc;
+}
+
+// Per-lane source offsets of this wave's LDS-DMA instructions. Instruction i (1 KiB,
+// 64 lanes x 16 B, lane-linear in LDS) is issued by wave i % 8; LDS chunk position
+// p = 72u + pc holds logical chunk ch = pc ^ swz(u) of token u.
+__device__ __forceinline__ uint32_t dma_voff(int wave, int n, int lane) {
+  const int i = wave + 8 * n;
+  const int p = 64 * i + lane;
+  const int u = p / 72, pc = p - 72 * u;
+  const int ch = (pc & ~7) | ((pc & 7) ^ swz(u));
+  return (uint32_t)(u * kRowBytes + 16 * ch);
+}
+
+// One of this wave's LDS-DMA instructions of a step (n < kDmaBase, or n == kDmaBase for
+// waves below kDmaWavesLong). The per-lane offset is recomputed at every issue from an
+// opaque copy of the lane id: kept live across the loop it gets spilled, and a scratch
+// reload waits vmcnt(0), which would drain the ring.
+__device__ __forceinline__ void issue_one(const i32x4& rsrc, uint32_t lds_slot, int n, int lane, int wave) {
+  if (n == kDmaBase && wave >= kDmaWavesLong) return;
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  lds_dma_x4(lds_slot + 1024u * (uint32_t)(wave + 8 * n), dma_voff(wave, n, l), rsrc);
+}
+
+__device__ __forceinline__ void issue_step(const i32x4& rsrc, uint32_t lds_slot, int lane, int wave) {
 #pragma unroll
-    for (int n = 0; n < kDmaBase + 1; ++n) {
-      const int i = wave + 8 * n;
-      if (n == kDmaBase && wave >= kDmaWavesLong) break;
-      const int p = 64 * i + lane;
-      const int u = p / 72, pc = p - 72 * u;
-      const int ch = (pc & ~7) | ((pc & 7) ^ swz(u));
-      const uint32_t voff = (uint32_t)(u * kRowBytes + 16 * ch);
-      lds_dma_x4(lds_base + 1024u * (uint32_t)i, voff, rsrc);
-    }
-  }
-};
+  for (int n = 0; n < kDmaBase + 1; ++n) issue_one(rsrc, lds_slot, n, lane, wave);
+}
+
+constexpr int kQkAhead = 4;   // score-operand reads in flight ahead of the MFMA consuming them
+
+// LDS byte offset (inside a slot) of score tile t: token tile t%2, 32-channel k-step t/2
+__device__ __forceinline__ int qk_off(const int* qk_b, int t) {
+  const int ks = t >> 1, mt = t & 1;
+  return mt * 16 * kRowBytes + qk_b[ks & 1] + 128 * (ks >> 1);
+}
 
 __device__ __forceinline__ bf16x8 lds_b128(const char __attribute__((address_space(3)))* p) {
   u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)p;
@@ -210,7 +241,7 @@ __device__ __forceinline__ float sum_across_quarters(float x) {
 
 
 template <bool kFp8>
-__global__ __launch_bounds__(kThreads, 1) void decode_kernel(
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(
     const __bf16* __restrict__ q_ptr, const char* __restrict__ kv_ptr, const float* __restrict__ kv_scales,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
     const int32_t* __restrict__ plan, float* __restrict__ ws, float* __restrict__ out_ptr,
@@ -230,20 +261,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(
   k_last = k_last < n_items - 1 ? k_last : n_items - 1;
   if (kb >= n_items || k_last < kb) return;
 
-  // ---- per-lane LDS addressing (byte offsets inside a ring slot)
+  // ---- per-lane LDS addressing (byte offsets inside a ring slot), rebuilt from an opaque
+  // lane id at the start of each use so that it does not occupy registers across the loop
   // scores, A = Z[16 tokens x 32 channels]: lane reads token l%16, chunk 4ks + l/16
   // chunk ch = 4ks + g (g = lane>>4) sits at (ch & ~7) | ((ch & 7) ^ swz(token)); swz(u) == swz(u+16)
-  int qk_b[2];
-  {
-    const int tok = lane & 15, g = lane >> 4;
+  auto qk_addr = [&](int* qk_b) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    const int tok = l & 15, g = l >> 4;
 #pragma unroll
     for (int x = 0; x < 2; ++x) qk_b[x] = tok * kRowBytes + 16 * ((4 * x + g) ^ swz(tok));
-  }
+  };
   // values, A = Z^T via transposing reads: lane j of 16-lane group G reads token
   // 16q + 8(G>>1) + 4e + (j>>2), channels 64w + 32mt + 16(G&1) + 4(j&3) .. +3
-  int pv_base[2][2];   // [token half e][channel tile mt]
-  {
-    const int G = lane >> 4, j = lane & 15;
+  auto pv_addr = [&](int (*pv_base)[2]) {   // [token half e][channel tile mt]
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    const int G = l >> 4, j = l & 15;
     const int u0 = 8 * (G >> 1) + (j >> 2);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
@@ -253,79 +287,93 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(
         const int ch = 8 * wave + 4 * mt + 2 * (G & 1) + ((j & 3) >> 1);   // 16-B chunk index
         pv_base[e][mt] = u * kRowBytes + 16 * ((ch & ~7) | ((ch & 7) ^ swz(u))) + 8 * (j & 1);
       }
-  }
+  };
   char __attribute__((address_space(3)))* pbuf = lds + kOffP;
   float __attribute__((address_space(3)))* alpha_s = (float __attribute__((address_space(3)))*)(lds + kOffAlpha);
-  int __attribute__((address_space(3)))* flag_s = (int __attribute__((address_space(3)))*)(lds + kOffFlag);
   float __attribute__((address_space(3)))* stat_m = (float __attribute__((address_space(3)))*)(lds + kOffStat);
   float __attribute__((address_space(3)))* stat_l = stat_m + kRowsPerTile;
 
-  // ---- prologue: issue the first kNBuf-1 steps
-  auto settle = [&](LoadCursor& c) {
-    while (c.k <= k_last && c.hh >= c.hh1) {
-      ++c.k;
-      if (c.k > k_last) break;
-      const Seg s = seg_of(plan, c.k, kb, pb, ke, pe);
-      c.hh = s.hh0; c.hh1 = s.hh1;
+  const int rows_total = a.s_q * a.heads;
+  // Q^T B-operand (16x16x32) of item k: lane holds query row 16*wave + (lane & 15) of the
+  // item's tile, channels 32ks + 8(lane>>4) .. +7. The next item's rows are loaded right
+  // after the current item's finalize.
+  bf16x8 qreg[18];
+  int q_item = -1;
+  auto load_q = [&](int k) {
+    int l = lane;   // opaque: a hoisted per-lane address would be spilled
+    asm volatile("" : "+v"(l));
+    const int32_t* it = plan + plan_items_off() + kItemWords * k;
+    const int g_row = kRowsPerTile * it[kITile] + 16 * wave + (l & 15);
+    const bool ok = g_row < rows_total;
+    const int jt = ok ? g_row / a.heads : 0;
+    const int hd = ok ? g_row - jt * a.heads : 0;
+    // rows past the last query row (a partial tile) compute with a copy of the tile's first
+    // row: every output column of the MFMAs depends on its own row only, and the finalize
+    // writes no such row
+    const __bf16* qrow = q_ptr + ((int64_t)(it[kISeq] * a.s_q + jt) * a.heads + hd) * kDqk + 8 * (l >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    q_item = k;
+  };
+  load_q(kb);
+
+  // ---- load cursor; the first kNBuf-1 steps are issued up front, then one step per
+  // compute region (its DMA instructions spread between the score MFMAs)
+  LoadCursor lc;
+  cursor_enter(lc, plan, kb, kb, pb, ke, pe);
+  auto settle = [&]() {
+    while (lc.k <= k_last && lc.hh >= lc.hh1) {
+      if (lc.k == k_last) {
+        lc.k = k_last + 1;
+        break;
+      }
+      cursor_enter(lc, plan, lc.k + 1, kb, pb, ke, pe);
     }
   };
-  LoadCursor lc;
-  {
-    const Seg s0 = seg_of(plan, kb, kb, pb, ke, pe);
-    lc.k = kb; lc.hh = s0.hh0; lc.hh1 = s0.hh1;
-  }
-  settle(lc);
+  settle();
+  if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
   int load_slot = 0;
   int issued_ahead = 0;   // steps issued whose data the compute loop has not consumed yet
+  auto advance = [&]() {
+    ++issued_ahead;
+    load_slot = (load_slot + 1) & (kNBuf - 1);
+    ++lc.hh;
+    settle();
+    if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
+  };
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
 #pragma unroll 1
   for (int i = 0; i < kNBuf - 1; ++i) {
     if (lc.k <= k_last) {
-      Loader<kFp8>::issue(a, kv_ptr, block_table, plan, lc.k, lc.hh, lds + load_slot * kBufBytes, lane, wave);
-      ++issued_ahead;
-      load_slot = (load_slot + 1) & (kNBuf - 1);
-      ++lc.hh;
-      settle(lc);
+      issue_step(cursor_rsrc(lc, a, kv_ptr), lds_u32 + load_slot * kBufBytes, lane, wave);
+      advance();
     }
   }
 
   int comp_slot = 0;
-  const int rows_total = a.s_q * a.heads;
 
 #pragma unroll 1
   for (int k = kb; k <= k_last; ++k) {
     const Seg sg = seg_of(plan, k, kb, pb, ke, pe);
     const int32_t* it = plan + plan_items_off() + kItemWords * k;
-    const int seq = it[kISeq], tile = it[kITile];
-    const int nsplits = it[kINsplits], slot_base = it[kISlot], owner = it[kIOwner];
 
-    // ---- this lane's query row for scores: row 16*wave + (lane & 15)
-    const int my_row = 16 * wave + (lane & 15);
-    const int g_row = kRowsPerTile * tile + my_row;
-    const bool row_ok = g_row < rows_total;
-    const int j_tok = row_ok ? g_row / a.heads : 0;
-    const int head = row_ok ? g_row - j_tok * a.heads : 0;
+    // ---- number of keys visible to this lane's query row (16*wave + (lane & 15))
     int lim = 0;
-    if (row_ok) {
-      int t = seqlens[seq];
-      t = t < 0 ? 0 : t;
-      const int cap = a.max_pages * kPage;
-      t = t > cap ? cap : t;
-      lim = t;
-      if (a.causal) {
-        lim = t - a.s_q + 1 + j_tok;
-        lim = lim < 0 ? 0 : (lim > t ? t : lim);
+    {
+      const int g_row = kRowsPerTile * it[kITile] + 16 * wave + (lane & 15);
+      if (g_row < rows_total) {
+        int t = seqlens[it[kISeq]];
+        t = t < 0 ? 0 : t;
+        const int cap = a.max_pages * kPage;
+        t = t > cap ? cap : t;
+        lim = t;
+        if (a.causal) {
+          lim = t - a.s_q + 1 + g_row / a.heads;
+          lim = lim < 0 ? 0 : (lim > t ? t : lim);
+        }
       }
     }
-    // Q^T B-operand (16x16x32): lane holds row (lane&15), channels 32ks + 8(lane>>4) .. +7
-    bf16x8 qreg[18];
-    {
-      const __bf16* qrow = q_ptr +
-                           ((int64_t)(seq * a.s_q + j_tok) * a.heads + head) * kDqk + 8 * (lane >> 4);
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks)
-        qreg[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 32 * ks) : bf16x8{};
-    }
-    wait_vmcnt<0>();
+    if (q_item != k) load_q(k);   // (after an item with no steps)
 
     f32x16 oacc[2][4];
 #pragma unroll
@@ -334,10 +382,134 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(
       for (int nt = 0; nt < 4; ++nt) oacc[mt][nt] = f32x16{};
     float m_run = -INFINITY;   // log2 domain
     float l_run = 0.f;
+    const int nsteps = sg.hh1 - sg.hh0;
 
-#pragma unroll 1
-    for (int hh = sg.hh0; hh < sg.hh1; ++hh) {
-      // wait for this step's data (later steps stay in flight), then make it visible
+    // --- pipeline pieces -------------------------------------------------------------
+    // scores of one step: S^T[32 tokens x 16 rows] as two 16x16 tiles; 36 tiles
+    // t = (k-step t/2, token tile t%2), operand reads kQkAhead tiles ahead of their MFMA
+    auto scores = [&](const char __attribute__((address_space(3)))* zb, f32x4* sacc, bool load, const i32x4& rs,
+                      uint32_t slot) {
+      sacc[0] = f32x4{};
+      sacc[1] = f32x4{};
+      int qk_b[2];
+      qk_addr(qk_b);
+      bf16x8 aring[kQkAhead];
+#pragma unroll
+      for (int t = 0; t < kQkAhead; ++t) aring[t] = lds_b128(zb + qk_off(qk_b, t));
+#pragma unroll
+      for (int t = 0; t < 36; ++t) {
+        const bf16x8 cur = aring[t % kQkAhead];
+        if (t + kQkAhead < 36) aring[t % kQkAhead] = lds_b128(zb + qk_off(qk_b, t + kQkAhead));
+        sacc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qreg[t >> 1], sacc[t & 1], 0, 0, 0);
+        if ((t & 7) == 0 && load) issue_one(rs, slot, t >> 3, lane, wave);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // mask + online softmax (log2 domain) of step hh; lane: row my_row, tokens
+    // 16mt + 4(lane>>4) + v. Returns P as bf16 and the row's rescale factor. Branch-free
+    // (the lazy rescale is a select), so it can be scheduled among the value MFMAs; with
+    // live == false it leaves the running state untouched.
+    auto softmax = [&](const f32x4* sacc, int hh, bool live, bf16x4* pk, float* alpha_out) {
+      const int key0 = kStep * hh + 4 * (lane >> 4);
+      float x[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float sv = sacc[mt][v] * a.scale_log2;
+          x[4 * mt + v] = (key0 + 16 * mt + v) < lim ? sv : -INFINITY;
+          mx = fmaxf(mx, x[4 * mt + v]);
+        }
+      mx = max_across_quarters(mx);
+      // move the reference max only when it grows by more than 2^kTau (O is still 0 while
+      // the reference is -inf, so no rescale is needed then)
+      const bool move = live && (mx > m_run + kTau);
+      const float alpha = (move && m_run != -INFINITY) ? exp2f(m_run - mx) : 1.f;
+      const float m_new = move ? mx : m_run;
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(x[i] - m_use);
+        psum += p;
+        pk[i >> 2][i & 3] = (__bf16)p;
+      }
+      psum = sum_across_quarters(psum);
+      const float l_new = alpha * l_run + psum;
+      m_run = m_new;
+      l_run = live ? l_new : l_run;
+      *alpha_out = alpha;
+    };
+    // addresses recomputed from an opaque lane id: kept live they would be spilled, and a
+    // scratch reload inside the step loop waits vmcnt(0) (draining the DMA ring)
+    auto publish = [&](const bf16x4* pk, float alpha) {
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      const int row = 16 * wave + (l & 15);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        *(bf16x4 __attribute__((address_space(3)))*)(pbuf + row * kPRowBytes + 2 * (16 * mt + 4 * (l >> 4))) = pk[mt];
+      if (l < 16) alpha_s[row] = alpha;
+    };
+    // O^T[64 channels of this wave][128 rows] = alpha O^T + Z^T P^T for one step; the
+    // softmax of the next step (VALU) is issued among these MFMAs
+    auto rescale = [&]() {
+      float al[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) al[nt] = alpha_s[32 * nt + (lane & 31)];
+      const bool any = __ballot(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) != 0;
+      if (any) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) oacc[mt][nt] *= al[nt];
+      }
+    };
+    auto values_and_softmax = [&](const char __attribute__((address_space(3)))* zb, const f32x4* sacc, int hh_next,
+                                  bool live, bf16x4* pk, float* alpha_out) {
+      // 8 (k-step q, row tile nt) pairs, 2 MFMAs each; P operands one pair ahead, the
+      // transposed Z^T operands of k-step 1 read during k-step 0
+      const char __attribute__((address_space(3)))* prow = pbuf + (lane & 31) * kPRowBytes + 16 * (lane >> 5);
+      int pv_base[2][2];
+      pv_addr(pv_base);
+      bf16x8 av[2][2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x4 lo = lds_tr16(zb + pv_base[0][mt]);
+        const bf16x4 hi = lds_tr16(zb + pv_base[1][mt]);
+        av[0][mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      bf16x8 bnext = lds_b128(prow);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = j >> 2, nt = j & 3;
+        const bf16x8 bp = bnext;
+        if (j + 1 < 8) bnext = lds_b128(prow + ((j + 1) & 3) * 32 * kPRowBytes + 32 * ((j + 1) >> 2));
+        if (j == 1) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const bf16x4 lo = lds_tr16(zb + kRowBytes * 16 + pv_base[0][mt]);
+            const bf16x4 hi = lds_tr16(zb + kRowBytes * 16 + pv_base[1][mt]);
+            av[1][mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[q][mt], bp, oacc[mt][nt], 0, 0, 0);
+      }
+      softmax(sacc, hh_next, live, pk, alpha_out);
+      // interleave: each value MFMA is followed by a few VALU (softmax) and one LDS read
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      }
+    };
+    // wait until this wave's DMA of the oldest unconsumed step has landed (younger
+    // steps stay in flight)
+    auto consume = [&]() {
       --issued_ahead;
       if (wave < kDmaWavesLong) {
         if (issued_ahead >= 2) wait_vmcnt<2 * (kDmaBase + 1)>();
@@ -348,204 +520,207 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(
         else if (issued_ahead == 1) wait_vmcnt<kDmaBase>();
         else wait_vmcnt<0>();
       }
-      barrier_lds();
-      // refill the slot freed by the previous step
-      if (lc.k <= k_last) {
-        Loader<kFp8>::issue(a, kv_ptr, block_table, plan, lc.k, lc.hh, lds + load_slot * kBufBytes, lane, wave);
-        ++issued_ahead;
-        load_slot = (load_slot + 1) & (kNBuf - 1);
-        ++lc.hh;
-        settle(lc);
-      }
-      const char __attribute__((address_space(3)))* zb = lds + comp_slot * kBufBytes;
+    };
+    // the step issued in a compute region goes into the slot freed by the barrier before it
+    auto load_next = [&](bool& load, i32x4& rs, uint32_t& slot) {
+      load = lc.k <= k_last;
+      rs = load ? cursor_rsrc(lc, a, kv_ptr) : i32x4{0, 0, 0, 0};
+      slot = lds_u32 + load_slot * kBufBytes;
+    };
 
-      // ---- scores S^T[32 tokens x 16 rows] as two 16x16 tiles
-      f32x4 sacc[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-      for (int ks = 0; ks < 18; ks += 2) {
-        bf16x8 av[2][2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            av[e][mt] = lds_b128(zb + mt * 16 * kRowBytes + qk_b[(ks + e) & 1] + 128 * ((ks + e) >> 1));
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[e][mt], qreg[ks + e], sacc[mt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // ---- mask + online softmax (log2 domain); lane: row my_row, tokens 16mt + 4(lane>>4) + v
-      const int key0 = kStep * hh + 4 * (lane >> 4);
-      float x[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int key = key0 + 16 * mt + v;
-          const float sv = sacc[mt][v] * a.scale_log2;
-          x[4 * mt + v] = key < lim ? sv : -INFINITY;
-          mx = fmaxf(mx, x[4 * mt + v]);
-        }
-      mx = max_across_quarters(mx);
-      float alpha = 1.f;
-      bool rescaled = false;
-      if (mx > m_run + kTau) {
-        alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - mx);
-        rescaled = m_run != -INFINITY;
-        m_run = mx;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float psum = 0.f;
+    // --- segment pipeline: after barrier B2(i), one region computes the scores of step
+    // i+1 and the value product of step i, then the softmax of step i+1 (its VALU work
+    // overlaps the value MFMAs still in flight), and issues the loads of a step kNBuf-1
+    // ahead into the slot freed at B1(i). Between B1(i+1) and B2(i+1) P/alpha of step i+1
+    // are published and the data of step i+2 is awaited.
+    if (nsteps > 0) {
+      f32x4 sacc[2];
       bf16x4 pk[2];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(x[i] - m_use);
-        psum += p;
-        pk[i >> 2][i & 3] = (__bf16)p;
+      float alpha = 1.f;
+      consume();                       // data of step 0
+      barrier_lds();                   // ... visible; previous segment fully done
+      const char __attribute__((address_space(3)))* zcur = lds + comp_slot * kBufBytes;
+      scores(zcur, sacc, false, i32x4{0, 0, 0, 0}, 0u);
+      softmax(sacc, sg.hh0, true, pk, &alpha);
+      publish(pk, alpha);
+      if (nsteps > 1) consume();       // data of step 1
+      barrier_lds();                   // B2(0)
+#pragma unroll 1
+      for (int i = 0; i < nsteps; ++i) {
+        const int cs_next = (comp_slot + 1) & (kNBuf - 1);
+        const char __attribute__((address_space(3)))* znext = lds + cs_next * kBufBytes;
+        const bool more = i + 1 < nsteps;
+        bool load;
+        i32x4 rs;
+        uint32_t lslot;
+        load_next(load, rs, lslot);
+        if (more) {
+          scores(znext, sacc, load, rs, lslot);
+        } else if (load) {
+          issue_step(rs, lslot, lane, wave);
+        }
+        if (load) advance();
+        rescale();
+        values_and_softmax(zcur, sacc, sg.hh0 + i + 1, more, pk, &alpha);
+        if (more) {
+          barrier_lds();               // B1(i+1): P(i), alpha(i) and step i's slot are free
+          publish(pk, alpha);
+          if (i + 2 < nsteps) consume();   // data of step i+2
+          barrier_lds();               // B2(i+1)
+        }
+        comp_slot = cs_next;
+        zcur = znext;
       }
-      psum = sum_across_quarters(psum);
-      l_run = alpha * l_run + psum;
-      // publish P as [row][token] (80-byte rows), alpha and the rescale flag
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        *(bf16x4 __attribute__((address_space(3)))*)(pbuf + my_row * kPRowBytes + 2 * (16 * mt + 4 * (lane >> 4))) =
-            pk[mt];
-      const uint64_t any = __ballot(rescaled);
-      if (lane < 16) alpha_s[my_row] = rescaled ? alpha : 1.f;
-      if (lane == 0) flag_s[wave] = any != 0;
-      barrier_lds();
+    }
 
-      // ---- O^T[64 channels of this wave][128 rows] += Z^T P^T
-      {
-        const u32x4 f0 = *(const u32x4 __attribute__((address_space(3)))*)flag_s;
-        const u32x4 f1 = *(const u32x4 __attribute__((address_space(3)))*)(flag_s + 4);
-        if ((f0[0] | f0[1] | f0[2] | f0[3] | f1[0] | f1[1] | f1[2] | f1[3]) != 0) {
+    // ---- finalize: exchange (m, l) per row, write out/lse or a partial. Addresses are
+    // rebuilt here from an opaque lane id and the plan record (kept live across the step
+    // loop they would be spilled, and a scratch reload waits for every load in flight).
+    {
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      const int32_t* itf = plan + plan_items_off() + kItemWords * k;
+      const int f_seq = itf[kISeq], f_tile = itf[kITile];
+      const bool split = itf[kINsplits] > 1;
+      const int slot = split ? itf[kISlot] + (worker - itf[kIOwner]) : 0;
+      const int mrow = 16 * wave + (l & 15);
+      if (l < 16) {
+        stat_m[mrow] = m_run;
+        stat_l[mrow] = l_run;
+      }
+      barrier_lds();
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const float al = alpha_s[32 * nt + (lane & 31)];
+      for (int nt = 0; nt < 4; ++nt) {
+        const int row = 32 * nt + (l & 31);
+        const int grow = kRowsPerTile * f_tile + row;
+        if (grow >= rows_total) continue;
+        const float lsum = stat_l[row];
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        const int jt = grow / a.heads, hd = grow - jt * a.heads;
+        float* dst = split ? (ws + (int64_t)slot * kSlotFloats + (int64_t)row * kLat)
+                           : (out_ptr + ((int64_t)(f_seq * a.s_q + jt) * a.heads + hd) * kLat);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) oacc[mt][nt] *= al;
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = 64 * wave + 32 * mt + 8 * g + 4 * (l >> 5);
+            f32x4 v;
+            v[0] = oacc[mt][nt][4 * g + 0] * inv;
+            v[1] = oacc[mt][nt][4 * g + 1] * inv;
+            v[2] = oacc[mt][nt][4 * g + 2] * inv;
+            v[3] = oacc[mt][nt][4 * g + 3] * inv;
+            *reinterpret_cast<f32x4*>(dst + c) = v;
           }
         }
       }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        bf16x8 av[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x4 lo = lds_tr16(zb + kRowBytes * 16 * q + pv_base[0][mt]);
-          const bf16x4 hi = lds_tr16(zb + kRowBytes * 16 * q + pv_base[1][mt]);
-          av[mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const bf16x8 bp = lds_b128(pbuf + (32 * nt + (lane & 31)) * kPRowBytes + 2 * (16 * q + 8 * (lane >> 5)));
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], bp, oacc[mt][nt], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      const int grow = kRowsPerTile * f_tile + mrow;
+      if (l < 16 && grow < rows_total) {
+        const float m = (m_run == -INFINITY) ? 0.f : m_run;
+        const float lse_v = l_run > 0.f ? (m + __log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+        const int jt = grow / a.heads, hd = grow - jt * a.heads;
+        if (split) ws[(int64_t)slot * kSlotFloats + (int64_t)kRowsPerTile * kLat + mrow] = lse_v;
+        else lse_ptr[(int64_t)(f_seq * a.s_q + jt) * a.heads + hd] = lse_v;
       }
-      comp_slot = (comp_slot + 1) & (kNBuf - 1);
+      barrier_lds();
     }
-
-    // ---- finalize: exchange (m, l) per row, write out/lse or a partial
-    if (lane < 16) {
-      stat_m[my_row] = m_run;
-      stat_l[my_row] = l_run;
-    }
-    barrier_lds();
-    const bool split = nsplits > 1;
-    const int slot = split ? slot_base + (worker - owner) : 0;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int row = 32 * nt + (lane & 31);
-      const int grow = kRowsPerTile * tile + row;
-      if (grow >= rows_total) continue;
-      const float l = stat_l[row];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int jt = grow / a.heads, hd = grow - jt * a.heads;
-      float* dst = split ? (ws + (int64_t)slot * kSlotFloats + (int64_t)row * kLat)
-                         : (out_ptr + ((int64_t)(seq * a.s_q + jt) * a.heads + hd) * kLat);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = 64 * wave + 32 * mt + 8 * g + 4 * (lane >> 5);
-          f32x4 v;
-          v[0] = oacc[mt][nt][4 * g + 0] * inv;
-          v[1] = oacc[mt][nt][4 * g + 1] * inv;
-          v[2] = oacc[mt][nt][4 * g + 2] * inv;
-          v[3] = oacc[mt][nt][4 * g + 3] * inv;
-          *reinterpret_cast<f32x4*>(dst + c) = v;
-        }
-      }
-    }
-    if (lane < 16 && row_ok) {
-      const float l = l_run;
-      const float m = (m_run == -INFINITY) ? 0.f : m_run;
-      const float lse_v = l > 0.f ? (m + __log2f(l)) * 0.6931471805599453f : -INFINITY;
-      if (split) ws[(int64_t)slot * kSlotFloats + (int64_t)kRowsPerTile * kLat + my_row] = lse_v;
-      else lse_ptr[(int64_t)(seq * a.s_q + j_tok) * a.heads + head] = lse_v;
-    }
-    barrier_lds();
+    // the next item's query rows: the youngest loads in flight, so waiting for them (at
+    // their first use) leaves no ring step behind
+    if (k < k_last) load_q(k + 1);
   }
 }
 
-// Merge the partials of split items: lse = log sum_k e^{lse_k}, out = sum_k e^{lse_k - lse} O_k.
+// Merge the partials of split items: lse = log sum_k e^{lse_k}, out = sum_k e^{lse_k - lse} O_k
+// (max-shifted; parts with lse = -inf carry no weight). One block per (split item, 16 rows):
+// the per-(row, split) weights are staged in LDS, then every thread streams float4 columns
+// of 8 rows with all 8 loads of a split in flight.
+constexpr int kCombRows = 16;
+constexpr int kCombMaxSplits = 256;
+
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ plan,
                                                       const float* __restrict__ ws, float* __restrict__ out,
                                                       float* __restrict__ lse, int s_q, int heads) {
+  __shared__ float wts[kCombRows][kCombMaxSplits];
   if (plan[kHMagic] != kPlanMagic) return;
   const int n_split = plan[kHSplitItems];
   const int n_items = plan[kHItems];
   if ((int)blockIdx.x >= n_split) return;
   const int k = plan[plan_split_off(n_items, plan[kHWorkers]) + blockIdx.x];
   const int32_t* it = plan + plan_items_off() + kItemWords * k;
-  const int seq = it[kISeq], tile = it[kITile], ns = it[kINsplits], slot0 = it[kISlot];
+  const int seq = it[kISeq], tile = it[kITile], ns_all = it[kINsplits], slot0 = it[kISlot];
   const int rows_total = s_q * heads;
-  const int sub = threadIdx.x >> 7;        // two rows per pass
-  const int c4 = (threadIdx.x & 127) * 4;  // channel quad
-  const int rows_per_block = kRowsPerTile / gridDim.y;
-  for (int r = blockIdx.y * rows_per_block + sub; r < (int)(blockIdx.y + 1) * rows_per_block; r += 2) {
-    const int grow = kRowsPerTile * tile + r;
-    if (grow >= rows_total) continue;
-    float m = -INFINITY;
-    for (int s = 0; s < ns; ++s) {
-      const float l = ws[(int64_t)(slot0 + s) * kSlotFloats + (int64_t)kRowsPerTile * kLat + r];
-      m = fmaxf(m, l);
+  const int r0 = blockIdx.y * kCombRows;
+  const int tid = threadIdx.x;
+  const int64_t lse_off = (int64_t)kRowsPerTile * kLat;
+  // splits are merged in chunks of kCombMaxSplits (one chunk in practice); the running
+  // (max, sum, acc) of earlier chunks is rescaled like the online softmax
+  const int c4 = (tid & 127) * 4;
+  const int rsub = tid >> 7;
+  f32x4 acc[8];
+  float tot[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { acc[j] = f32x4{0.f, 0.f, 0.f, 0.f}; tot[j] = 0.f; }
+  float mrow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mrow[j] = -INFINITY;
+  for (int s0 = 0; s0 < ns_all; s0 += kCombMaxSplits) {
+    const int ns = ns_all - s0 < kCombMaxSplits ? ns_all - s0 : kCombMaxSplits;
+    __syncthreads();
+    for (int idx = tid; idx < kCombRows * ns; idx += 256) {
+      const int r = idx / ns, sp = idx - r * ns;
+      wts[r][sp] = ws[(int64_t)(slot0 + s0 + sp) * kSlotFloats + lse_off + r0 + r];
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float tot = 0.f;
-    if (m != -INFINITY) {
-      for (int s = 0; s < ns; ++s) {
-        const float* base = ws + (int64_t)(slot0 + s) * kSlotFloats;
-        const float l = base[(int64_t)kRowsPerTile * kLat + r];
-        const float wgt = (l == -INFINITY) ? 0.f : __expf(l - m);
-        tot += wgt;
-        if (wgt != 0.f) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(base + (int64_t)r * kLat + c4);
-          acc += wgt * v;
-        }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = rsub + 2 * j;
+      float m = mrow[j];
+      for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, wts[r][sp]);
+      const float safe = m == -INFINITY ? 0.f : m;
+      const float resc = mrow[j] == -INFINITY ? 0.f : __expf(mrow[j] - safe);
+      acc[j] *= resc;
+      tot[j] *= resc;
+      mrow[j] = m;
+    }
+    for (int sp = 0; sp < ns; ++sp) {
+      const float* base = ws + (int64_t)(slot0 + s0 + sp) * kSlotFloats + c4;
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const f32x4*>(base + (int64_t)(r0 + rsub + 2 * j) * kLat);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float l = wts[rsub + 2 * j][sp];
+        const float wgt = l == -INFINITY ? 0.f : __expf(l - (mrow[j] == -INFINITY ? 0.f : mrow[j]));
+        tot[j] += wgt;
+        if (wgt != 0.f) acc[j] += wgt * v[j];
       }
     }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = r0 + rsub + 2 * j;
+    const int grow = kRowsPerTile * tile + r;
+    if (grow >= rows_total) continue;
     const int jt = grow / heads, hd = grow - jt * heads;
     const int64_t orow = (int64_t)(seq * s_q + jt) * heads + hd;
-    const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    *reinterpret_cast<f32x4*>(out + orow * kLat + c4) = acc * inv;
-    if (c4 == 0) lse[orow] = tot > 0.f ? m + __logf(tot) : -INFINITY;
+    const float inv = tot[j] > 0.f ? 1.f / tot[j] : 0.f;
+    *reinterpret_cast<f32x4*>(out + orow * kLat + c4) = acc[j] * inv;
+    if (c4 == 0) lse[orow] = tot[j] > 0.f ? mrow[j] + __logf(tot[j]) : -INFINITY;
   }
 }
 
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-  hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     kLdsBytes);
+  // the LDS opt-in is per device; remember it per device id
+  static thread_local int configured = -1;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  if (configured != dev) {
+    e = hipFuncSetAttribute((const void*)decode_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    configured = dev;
+  }
   hipLaunchKernelGGL(decode_kernel<false>, dim3(a.workers), dim3(kThreads), kLdsBytes, stream,
                      reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const char*>(a.kv), a.kv_scales,
                      a.block_table, a.seqlens, a.plan, a.ws, a.out, a.lse, scalars_of(a));
@@ -559,8 +734,8 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
   const int max_split = a.workers;   // split items <= active workers - 1
-  hipLaunchKernelGGL(combine_kernel, dim3(max_split, 8), dim3(256), 0, stream, a.plan, a.ws, a.out, a.lse, a.s_q,
-                     a.heads);
+  hipLaunchKernelGGL(combine_kernel, dim3(max_split, kRowsPerTile / kCombRows), dim3(256), 0, stream, a.plan, a.ws,
+                     a.out, a.lse, a.s_q, a.heads);
   return hipGetLastError();
 }
 

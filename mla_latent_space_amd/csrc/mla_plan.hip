@@ -4,7 +4,8 @@
 // scheduler balances sequence partitions across compute units so that 128-token and
 // 128k-token sequences in one batch leave no stragglers. This kernel is that idea on
 // gfx950: items (sequence, 128-row tile) are keyed by page count, sorted longest first
-// by a two-pass LSD radix sort in LDS (8-bit digits, wave ballots for the stable rank),
+// (up to 1024 items by a rank sort, beyond that by a two-pass LSD radix sort in LDS with
+// 8-bit digits and wave ballots for the stable rank),
 // costed as overhead + pages, prefix-summed, and cut into equal-cost contiguous runs,
 // one per worker (one persistent decode work-group per compute unit).
 #include "mla_internal.h"
@@ -87,50 +88,73 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
 
   uint32_t* src = keys_a;
   uint32_t* dst = keys_b;
-  for (int shift = 16; shift < 32; shift += 8) {
-    if (tid < 256) digit_base[tid] = 0;
-    for (int i = tid; i < kWaves * 256; i += kThreads) wave_cnt[i] = 0;
+  if (n <= kThreads) {
+    // Small batches: the packed keys are unique, so each item's position is the number of
+    // smaller keys (a rank sort; same order as the radix sort below).
+    const int n4 = (n + 3) & ~3;
+    if (tid >= n && tid < n4) keys_a[tid] = 0xFFFFFFFFu;   // pads compare greater than every key
     __syncthreads();
-    for (int i = tid; i < n; i += kThreads) atomicAdd(&digit_base[(src[i] >> shift) & 255], 1);
-    __syncthreads();
-    if (tid == 0) {
-      int run = 0;
-      for (int d = 0; d < 256; ++d) { const int c = digit_base[d]; digit_base[d] = run; run += c; }
+    const uint32_t mine = tid < n ? keys_a[tid] : 0u;
+    int rank = 0;
+    for (int j = 0; j < n4; j += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(keys_a + j);
+      rank += (v.x < mine) + (v.y < mine) + (v.z < mine) + (v.w < mine);
     }
+    if (tid < n) keys_b[rank] = mine;
     __syncthreads();
-    for (int t0 = 0; t0 < n; t0 += kThreads) {
-      const int i = t0 + tid;
-      const bool valid = i < n;
-      const uint32_t v = valid ? src[i] : 0u;
-      const int d = (int)((v >> shift) & 255);
-      uint64_t peers = __ballot(valid);
+    src = keys_b;
+    dst = keys_a;
+  } else {
+    // Two stable LSD passes over the 16-bit page key (8-bit digits). Within a tile of 1024
+    // items, the rank among equal digits comes from wave ballots; waves and tiles are
+    // ordered through per-digit counters.
+    for (int shift = 16; shift < 32; shift += 8) {
+      if (tid < 256) digit_base[tid] = 0;
+      for (int i = tid; i < kWaves * 256; i += kThreads) wave_cnt[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += kThreads) atomicAdd(&digit_base[(src[i] >> shift) & 255], 1);
+      __syncthreads();
+      {
+        int tot_unused = 0;
+        const int cnt = tid < 256 ? digit_base[tid] : 0;
+        const int excl = block_exclusive_scan(cnt, scratch, &tot_unused);
+        if (tid < 256) digit_base[tid] = excl;
+        __syncthreads();
+      }
+      for (int t0 = 0; t0 < n; t0 += kThreads) {
+        const int i = t0 + tid;
+        const bool valid = i < n;
+        const uint32_t v = valid ? src[i] : 0u;
+        const int d = (int)((v >> shift) & 255);
+        uint64_t peers = __ballot(valid);
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const uint64_t bb = __ballot((d >> b) & 1);
-        peers &= ((d >> b) & 1) ? bb : ~bb;
-      }
-      const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-      if (valid && rank == 0) wave_cnt[wave * 256 + d] = __popcll(peers);
-      __syncthreads();
-      if (tid < 256) {
-        int run = 0;
-        for (int w = 0; w < kWaves; ++w) {
-          const int c = wave_cnt[w * 256 + tid];
-          wave_cnt[w * 256 + tid] = run;
-          run += c;
+        for (int b = 0; b < 8; ++b) {
+          const uint64_t bb = __ballot((d >> b) & 1);
+          peers &= ((d >> b) & 1) ? bb : ~bb;
         }
-        tile_tot[tid] = run;
+        const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+        if (valid && rank == 0) wave_cnt[wave * 256 + d] = __popcll(peers);
+        __syncthreads();
+        if (tid < 256) {
+          int run = 0;
+          for (int w = 0; w < kWaves; ++w) {
+            const int c = wave_cnt[w * 256 + tid];
+            wave_cnt[w * 256 + tid] = run;
+            run += c;
+          }
+          tile_tot[tid] = run;
+        }
+        __syncthreads();
+        if (valid) dst[digit_base[d] + wave_cnt[wave * 256 + d] + rank] = v;
+        __syncthreads();
+        if (tid < 256) {
+          digit_base[tid] += tile_tot[tid];
+          for (int w = 0; w < kWaves; ++w) wave_cnt[w * 256 + tid] = 0;
+        }
+        __syncthreads();
       }
-      __syncthreads();
-      if (valid) dst[digit_base[d] + wave_cnt[wave * 256 + d] + rank] = v;
-      __syncthreads();
-      if (tid < 256) {
-        digit_base[tid] += tile_tot[tid];
-        for (int w = 0; w < kWaves; ++w) wave_cnt[w * 256 + tid] = 0;
-      }
-      __syncthreads();
+      uint32_t* tmp = src; src = dst; dst = tmp;
     }
-    uint32_t* tmp = src; src = dst; dst = tmp;
   }
   // src holds the sorted keys; dst becomes the cost prefix C_k.
   int* cost = reinterpret_cast<int*>(dst);
@@ -229,9 +253,15 @@ constexpr size_t kPlanLds = (size_t)2 * kMaxItems * 4 + (size_t)(kWaves * 256 + 
 hipError_t launch_plan(const int32_t* seqlens, int batch, int s_q, int heads, int causal, int workers,
                        int32_t* plan, hipStream_t stream) {
   static_assert(kPlanLds <= 160 * 1024, "plan LDS");
-  hipError_t e = hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)kPlanLds);
+  static thread_local int configured = -1;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  if (configured != dev) {
+    e = hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPlanLds);
+    if (e != hipSuccess) return e;
+    configured = dev;
+  }
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), kPlanLds, stream, seqlens, batch, s_q, heads, causal,
                      workers, plan);
   return hipGetLastError();
