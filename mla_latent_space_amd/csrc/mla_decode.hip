@@ -47,15 +47,32 @@ constexpr int kNBuf = 4;                       // LDS ring depth
 constexpr int kRowBytes = kDqk * 2;            // 1152
 constexpr int kBufBytes = kStep * kRowBytes;   // 36864
 constexpr int kDmaInstr = kBufBytes / 1024;    // 36 LDS-DMA instructions (1 KiB each) per step
-constexpr int kDmaBase = kDmaInstr / 8;        // 4 per wave ...
-constexpr int kDmaWavesLong = kDmaInstr % 8;   // ... and one more for waves 0..3
 constexpr int kPRowBytes = 80;                 // P exchange row: 32 bf16 + 16 B pad (bank spread)
-constexpr int kOffP = kNBuf * kBufBytes;       // P exchange: [128 rows][32 tokens] bf16
-constexpr int kOffAlpha = kOffP + kRowsPerTile * kPRowBytes;  // 128 floats: per-row rescale of this step
-constexpr int kOffFlag = kOffAlpha + 512;      // 8 ints: a wave rescaled this step
-constexpr int kOffStat = kOffFlag + 32;        // 128 floats m, 128 floats l
-constexpr int kLdsBytes = kOffStat + 1024;
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+// fp8 cache (OCP e4m3fn): a cached row is 512 codes + 64 bf16 rope channels (640 B), with
+// one f32 scale per 128-channel tile of the 512 latent channels in a separate array.
+constexpr int kF8Row = kLat + 2 * kRope;       // 640
+constexpr int kF8StepBytes = kStep * kF8Row;   // 20480: a half page of codes+rope, contiguous
+constexpr int kF8SlotBytes = kF8StepBytes + kStep * 16;   // + the step's 32 x 4 scales
+constexpr int kF8Slots = 3;                    // fp8 staging ring depth
+constexpr int kF8DmaInstr = kF8StepBytes / 1024 + 1;      // 20 row instructions + 1 for the scales
+
+// LDS layout. bf16 cache: a ring of kNBuf slots of 32 bf16 rows, read in place. fp8 cache:
+// a ring of kF8Slots staging slots (codes, rope, scales as loaded) and two bf16 slots that
+// each step is dequantised into once, so the score/value code is shared with the bf16 path.
+template <bool kFp8>
+struct Lds {
+  static constexpr int kWork = kFp8 ? 2 : kNBuf;                      // bf16 slots
+  static constexpr int kOffF8 = kWork * kBufBytes;                    // fp8 staging ring
+  static constexpr int kOffP = kOffF8 + (kFp8 ? kF8Slots * kF8SlotBytes : 0);   // P: [128 rows][32 tokens] bf16
+  static constexpr int kOffAlpha = kOffP + kRowsPerTile * kPRowBytes;  // 128 floats: per-row rescale of a step
+  static constexpr int kOffStat = kOffAlpha + 512;                    // 128 floats m, 128 floats l
+  static constexpr int kBytes = kOffStat + 1024;
+  static_assert(kBytes <= 160 * 1024, "LDS budget");
+  // LDS-DMA instructions per step: waves below kLong issue kBase + 1, the others kBase
+  static constexpr int kDmaBase = kFp8 ? kF8DmaInstr / 8 : kDmaInstr / 8;
+  static constexpr int kLong = kFp8 ? kF8DmaInstr % 8 : kDmaInstr % 8;
+  static constexpr int kIssueEvery = 36 / (kDmaBase + 1);   // score tiles between two DMA instructions
+};
 constexpr float kTau = 8.0f;                   // lazy rescale threshold (log2 units)
 constexpr uint32_t kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit format, gfx9 family
 
@@ -158,22 +175,42 @@ __device__ __forceinline__ void cursor_enter(LoadCursor& c, const int32_t* __res
   c.hh1 = sg.hh1;
 }
 
-// Buffer descriptor of the cursor's step (32 tokens = half of a 64-token page): base at the
-// step's first row, record count at the last visible token, so rows past it read as zeros.
-// A page id outside [0, num_pages) gives 0 records (all zeros).
-__device__ __forceinline__ i32x4 cursor_rsrc(const LoadCursor& c, const Scalars& a, const char* __restrict__ kv) {
+// Buffer descriptors of the cursor's step (32 tokens = half of a 64-token page): base at
+// the step's first row, record count at the last visible token, so rows past it read as
+// zeros. A page id outside [0, num_pages) gives 0 records (all zeros). For an fp8 cache the
+// second descriptor covers the step's scales. (Uniform by construction; readfirstlane tells
+// the compiler so, keeping them in SGPRs.)
+struct StepRsrc {
+  i32x4 kv, sc;
+};
+
+__device__ __forceinline__ i32x4 make_rsrc(uint64_t addr, int bytes) {
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(addr >> 32) & 0xFFFF));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);                                    // num_records
+  r[3] = (int)kRsrcWord3;
+  return r;
+}
+
+template <bool kFp8>
+__device__ __forceinline__ StepRsrc cursor_rsrc(const LoadCursor& c, const Scalars& a, const char* __restrict__ kv,
+                                                const float* __restrict__ scales) {
   int valid = c.vis - kStep * c.hh;
   valid = valid > kStep ? kStep : valid;
   const bool ok = c.pid >= 0 && (int64_t)c.pid < a.num_pages && valid > 0;
-  const uint64_t addr = reinterpret_cast<uint64_t>(kv) +
-                        (ok ? ((uint64_t)c.pid * (kPage * kRowBytes) + (uint64_t)(c.hh & 1) * kBufBytes) : 0);
-  // (uniform by construction; readfirstlane tells the compiler so, keeping it in SGPRs)
-  i32x4 rsrc;
-  rsrc[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
-  rsrc[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(addr >> 32) & 0xFFFF));   // stride 0
-  rsrc[2] = __builtin_amdgcn_readfirstlane(ok ? valid * kRowBytes : 0);              // num_records
-  rsrc[3] = (int)kRsrcWord3;
-  return rsrc;
+  StepRsrc r;
+  if constexpr (!kFp8) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(kv) +
+                          (ok ? ((uint64_t)c.pid * (kPage * kRowBytes) + (uint64_t)(c.hh & 1) * kBufBytes) : 0);
+    r.kv = make_rsrc(addr, ok ? valid * kRowBytes : 0);
+    r.sc = r.kv;
+  } else {
+    const uint64_t tok0 = ok ? (uint64_t)c.pid * kPage + (uint64_t)(c.hh & 1) * kStep : 0;
+    r.kv = make_rsrc(reinterpret_cast<uint64_t>(kv) + tok0 * kF8Row, ok ? valid * kF8Row : 0);
+    r.sc = make_rsrc(reinterpret_cast<uint64_t>(scales) + tok0 * 16, ok ? valid * 16 : 0);
+  }
+  return r;
 }
 
 // Per-lane source offsets of this wave's LDS-DMA instructions. Instruction i (1 KiB,
@@ -187,20 +224,77 @@ __device__ __forceinline__ uint32_t dma_voff(int wave, int n, int lane) {
   return (uint32_t)(u * kRowBytes + 16 * ch);
 }
 
-// One of this wave's LDS-DMA instructions of a step (n < kDmaBase, or n == kDmaBase for
-// waves below kDmaWavesLong). The per-lane offset is recomputed at every issue from an
-// opaque copy of the lane id: kept live across the loop it gets spilled, and a scratch
-// reload waits vmcnt(0), which would drain the ring.
-__device__ __forceinline__ void issue_one(const i32x4& rsrc, uint32_t lds_slot, int n, int lane, int wave) {
-  if (n == kDmaBase && wave >= kDmaWavesLong) return;
+// One of this wave's LDS-DMA instructions of a step: instruction i = wave + 8n. The per-lane
+// offset is recomputed at every issue from an opaque copy of the lane id: kept live across
+// the loop it gets spilled, and a scratch reload waits vmcnt(0), which would drain the ring.
+// bf16: 36 instructions of 1 KiB into the swizzled slot. fp8: 20 instructions copy the
+// step's 20 KiB of codes+rope as they are, the 21st (lanes 0..31) its 512 B of scales.
+template <bool kFp8>
+__device__ __forceinline__ void issue_one(const StepRsrc& rs, uint32_t lds_slot, int n, int lane, int wave) {
+  const int i = wave + 8 * n;
   int l = lane;
   asm volatile("" : "+v"(l));
-  lds_dma_x4(lds_slot + 1024u * (uint32_t)(wave + 8 * n), dma_voff(wave, n, l), rsrc);
+  if constexpr (!kFp8) {
+    if (i >= kDmaInstr) return;
+    lds_dma_x4(lds_slot + 1024u * (uint32_t)i, dma_voff(wave, n, l), rs.kv);
+  } else {
+    if (i >= kF8DmaInstr) return;
+    if (i < kF8DmaInstr - 1) {
+      lds_dma_x4(lds_slot + 1024u * (uint32_t)i, 1024u * (uint32_t)i + 16u * (uint32_t)l, rs.kv);
+    } else if (l < kStep) {
+      lds_dma_x4(lds_slot + (uint32_t)kF8StepBytes, 16u * (uint32_t)l, rs.sc);
+    }
+  }
 }
 
-__device__ __forceinline__ void issue_step(const i32x4& rsrc, uint32_t lds_slot, int lane, int wave) {
+template <bool kFp8>
+__device__ __forceinline__ void issue_step(const StepRsrc& rs, uint32_t lds_slot, int lane, int wave) {
 #pragma unroll
-  for (int n = 0; n < kDmaBase + 1; ++n) issue_one(rsrc, lds_slot, n, lane, wave);
+  for (int n = 0; n < Lds<kFp8>::kDmaBase + 1; ++n) issue_one<kFp8>(rs, lds_slot, n, lane, wave);
+}
+
+// Dequantise one fp8 step from its staging slot into a bf16 slot (same row layout and
+// swizzle as a bf16 cache step): thread t handles token t/16 and latent channels
+// 32(t%16) .. +31, value = bf16(e4m3(code) * scale[token][tile]), plus 4 rope channels
+// copied as they are. Zero-filled rows (past the visible tokens) stay zero.
+__device__ __forceinline__ void dequant_step(const char __attribute__((address_space(3)))* f8,
+                                             char __attribute__((address_space(3)))* dst, int tid) {
+  asm volatile("" : "+v"(tid));
+  const int u = tid >> 4, cg = tid & 15;
+  const char __attribute__((address_space(3)))* row = f8 + u * kF8Row;
+  const u32x4 c0 = *(const u32x4 __attribute__((address_space(3)))*)(row + 32 * cg);
+  const u32x4 c1 = *(const u32x4 __attribute__((address_space(3)))*)(row + 32 * cg + 16);
+  const float sc = *(const float __attribute__((address_space(3)))*)(f8 + kF8StepBytes + 16 * u + 4 * (cg >> 2));
+  const uint32_t rope_lo = *(const uint32_t __attribute__((address_space(3)))*)(row + kLat + 8 * cg);
+  const uint32_t rope_hi = *(const uint32_t __attribute__((address_space(3)))*)(row + kLat + 8 * cg + 4);
+  uint32_t w[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+  bf16x2 o[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[j], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[j], true);
+    o[2 * j][0] = (__bf16)(lo[0] * sc);
+    o[2 * j][1] = (__bf16)(lo[1] * sc);
+    o[2 * j + 1][0] = (__bf16)(hi[0] * sc);
+    o[2 * j + 1][1] = (__bf16)(hi[1] * sc);
+  }
+  char __attribute__((address_space(3)))* drow = dst + u * kRowBytes;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int ch = 4 * cg + c;   // logical 16-B chunk of the 1152-B row
+    u32x4 v;
+    v[0] = __builtin_bit_cast(uint32_t, o[4 * c + 0]);
+    v[1] = __builtin_bit_cast(uint32_t, o[4 * c + 1]);
+    v[2] = __builtin_bit_cast(uint32_t, o[4 * c + 2]);
+    v[3] = __builtin_bit_cast(uint32_t, o[4 * c + 3]);
+    *(u32x4 __attribute__((address_space(3)))*)(drow + 16 * ((ch & ~7) | ((ch & 7) ^ swz(u)))) = v;
+  }
+  // rope: logical bytes 1024 + 8cg = chunk 64 + cg/2, half cg&1
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  u32x2 r;
+  r[0] = rope_lo;
+  r[1] = rope_hi;
+  *(u32x2 __attribute__((address_space(3)))*)(drow + 16 * (64 + ((cg >> 1) ^ swz(u))) + 8 * (cg & 1)) = r;
 }
 
 constexpr int kQkAhead = 4;   // score-operand reads in flight ahead of the MFMA consuming them
@@ -288,9 +382,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
         pv_base[e][mt] = u * kRowBytes + 16 * ((ch & ~7) | ((ch & 7) ^ swz(u))) + 8 * (j & 1);
       }
   };
-  char __attribute__((address_space(3)))* pbuf = lds + kOffP;
-  float __attribute__((address_space(3)))* alpha_s = (float __attribute__((address_space(3)))*)(lds + kOffAlpha);
-  float __attribute__((address_space(3)))* stat_m = (float __attribute__((address_space(3)))*)(lds + kOffStat);
+  using L = Lds<kFp8>;
+  char __attribute__((address_space(3)))* pbuf = lds + L::kOffP;
+  float __attribute__((address_space(3)))* alpha_s = (float __attribute__((address_space(3)))*)(lds + L::kOffAlpha);
+  float __attribute__((address_space(3)))* stat_m = (float __attribute__((address_space(3)))*)(lds + L::kOffStat);
   float __attribute__((address_space(3)))* stat_l = stat_m + kRowsPerTile;
 
   const int rows_total = a.s_q * a.heads;
@@ -317,8 +412,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
   };
   load_q(kb);
 
-  // ---- load cursor; the first kNBuf-1 steps are issued up front, then one step per
-  // compute region (its DMA instructions spread between the score MFMAs)
+  // ---- load cursor; the first kLoadSlots-1 (bf16) or kLoadSlots (fp8) steps are issued
+  // up front, then one step per compute region (its DMA instructions spread between the
+  // score MFMAs)
+  constexpr int kLoadSlots = kFp8 ? kF8Slots : kNBuf;
+  constexpr int kLoadBase = kFp8 ? L::kOffF8 : 0;
+  constexpr int kLoadSlotBytes = kFp8 ? kF8SlotBytes : kBufBytes;
   LoadCursor lc;
   cursor_enter(lc, plan, kb, kb, pb, ke, pe);
   auto settle = [&]() {
@@ -336,21 +435,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
   int issued_ahead = 0;   // steps issued whose data the compute loop has not consumed yet
   auto advance = [&]() {
     ++issued_ahead;
-    load_slot = (load_slot + 1) & (kNBuf - 1);
+    load_slot = load_slot + 1 == kLoadSlots ? 0 : load_slot + 1;
     ++lc.hh;
     settle();
     if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
   };
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
 #pragma unroll 1
-  for (int i = 0; i < kNBuf - 1; ++i) {
+  for (int i = 0; i < (kFp8 ? kF8Slots : kNBuf - 1); ++i) {
     if (lc.k <= k_last) {
-      issue_step(cursor_rsrc(lc, a, kv_ptr), lds_u32 + load_slot * kBufBytes, lane, wave);
+      issue_step<kFp8>(cursor_rsrc<kFp8>(lc, a, kv_ptr, kv_scales), lds_u32 + kLoadBase + load_slot * kLoadSlotBytes,
+                       lane, wave);
       advance();
     }
   }
 
-  int comp_slot = 0;
+  int comp_slot = 0;   // bf16 slot of the segment's current step
+  int conv_slot = 0;   // fp8: staging slot of the next step to dequantise
 
 #pragma unroll 1
   for (int k = kb; k <= k_last; ++k) {
@@ -387,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
     // --- pipeline pieces -------------------------------------------------------------
     // scores of one step: S^T[32 tokens x 16 rows] as two 16x16 tiles; 36 tiles
     // t = (k-step t/2, token tile t%2), operand reads kQkAhead tiles ahead of their MFMA
-    auto scores = [&](const char __attribute__((address_space(3)))* zb, f32x4* sacc, bool load, const i32x4& rs,
+    auto scores = [&](const char __attribute__((address_space(3)))* zb, f32x4* sacc, bool load, const StepRsrc& rs,
                       uint32_t slot) {
       sacc[0] = f32x4{};
       sacc[1] = f32x4{};
@@ -401,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
         const bf16x8 cur = aring[t % kQkAhead];
         if (t + kQkAhead < 36) aring[t % kQkAhead] = lds_b128(zb + qk_off(qk_b, t + kQkAhead));
         sacc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qreg[t >> 1], sacc[t & 1], 0, 0, 0);
-        if ((t & 7) == 0 && load) issue_one(rs, slot, t >> 3, lane, wave);
+        if (t % L::kIssueEvery == 0 && load) issue_one<kFp8>(rs, slot, t / L::kIssueEvery, lane, wave);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -511,21 +612,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
     // steps stay in flight)
     auto consume = [&]() {
       --issued_ahead;
-      if (wave < kDmaWavesLong) {
-        if (issued_ahead >= 2) wait_vmcnt<2 * (kDmaBase + 1)>();
-        else if (issued_ahead == 1) wait_vmcnt<kDmaBase + 1>();
+      if (wave < L::kLong) {
+        if (issued_ahead >= 2) wait_vmcnt<2 * (L::kDmaBase + 1)>();
+        else if (issued_ahead == 1) wait_vmcnt<L::kDmaBase + 1>();
         else wait_vmcnt<0>();
       } else {
-        if (issued_ahead >= 2) wait_vmcnt<2 * kDmaBase>();
-        else if (issued_ahead == 1) wait_vmcnt<kDmaBase>();
+        if (issued_ahead >= 2) wait_vmcnt<2 * L::kDmaBase>();
+        else if (issued_ahead == 1) wait_vmcnt<L::kDmaBase>();
         else wait_vmcnt<0>();
       }
     };
+    // fp8: dequantise the oldest staged step into bf16 slot ws
+    auto dequant = [&](int wslot) {
+      dequant_step(lds + L::kOffF8 + conv_slot * kF8SlotBytes, lds + wslot * kBufBytes, (int)threadIdx.x);
+      conv_slot = conv_slot + 1 == kF8Slots ? 0 : conv_slot + 1;
+    };
     // the step issued in a compute region goes into the slot freed by the barrier before it
-    auto load_next = [&](bool& load, i32x4& rs, uint32_t& slot) {
+    auto load_next = [&](bool& load, StepRsrc& rs, uint32_t& slot) {
       load = lc.k <= k_last;
-      rs = load ? cursor_rsrc(lc, a, kv_ptr) : i32x4{0, 0, 0, 0};
-      slot = lds_u32 + load_slot * kBufBytes;
+      if (load) rs = cursor_rsrc<kFp8>(lc, a, kv_ptr, kv_scales);
+      slot = lds_u32 + kLoadBase + load_slot * kLoadSlotBytes;
     };
 
     // --- segment pipeline: after barrier B2(i), one region computes the scores of step
@@ -537,36 +643,58 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
       f32x4 sacc[2];
       bf16x4 pk[2];
       float alpha = 1.f;
-      consume();                       // data of step 0
-      barrier_lds();                   // ... visible; previous segment fully done
+      const StepRsrc no_rs = {};
       const char __attribute__((address_space(3)))* zcur = lds + comp_slot * kBufBytes;
-      scores(zcur, sacc, false, i32x4{0, 0, 0, 0}, 0u);
-      softmax(sacc, sg.hh0, true, pk, &alpha);
-      publish(pk, alpha);
-      if (nsteps > 1) consume();       // data of step 1
-      barrier_lds();                   // B2(0)
+      if constexpr (!kFp8) {
+        consume();                     // data of step 0
+        barrier_lds();                 // ... visible; previous segment fully done
+        scores(zcur, sacc, false, no_rs, 0u);
+        softmax(sacc, sg.hh0, true, pk, &alpha);
+        publish(pk, alpha);
+        if (nsteps > 1) consume();     // data of step 1
+        barrier_lds();                 // B2(0)
+      } else {
+        consume();                     // staged data of steps 0 and 1
+        if (nsteps > 1) consume();
+        barrier_lds();
+        dequant(comp_slot);
+        if (nsteps > 1) dequant(comp_slot ^ 1);
+        barrier_lds();
+        scores(zcur, sacc, false, no_rs, 0u);
+        softmax(sacc, sg.hh0, true, pk, &alpha);
+        publish(pk, alpha);
+        barrier_lds();                 // B2(0)
+      }
 #pragma unroll 1
       for (int i = 0; i < nsteps; ++i) {
-        const int cs_next = (comp_slot + 1) & (kNBuf - 1);
+        const int cs_next = comp_slot + 1 == L::kWork ? 0 : comp_slot + 1;
         const char __attribute__((address_space(3)))* znext = lds + cs_next * kBufBytes;
         const bool more = i + 1 < nsteps;
         bool load;
-        i32x4 rs;
+        StepRsrc rs;
         uint32_t lslot;
         load_next(load, rs, lslot);
         if (more) {
           scores(znext, sacc, load, rs, lslot);
         } else if (load) {
-          issue_step(rs, lslot, lane, wave);
+          issue_step<kFp8>(rs, lslot, lane, wave);
         }
         if (load) advance();
         rescale();
         values_and_softmax(zcur, sacc, sg.hh0 + i + 1, more, pk, &alpha);
         if (more) {
-          barrier_lds();               // B1(i+1): P(i), alpha(i) and step i's slot are free
-          publish(pk, alpha);
-          if (i + 2 < nsteps) consume();   // data of step i+2
-          barrier_lds();               // B2(i+1)
+          if constexpr (!kFp8) {
+            barrier_lds();             // B1(i+1): P(i), alpha(i) and step i's slot are free
+            publish(pk, alpha);
+            if (i + 2 < nsteps) consume();   // data of step i+2
+            barrier_lds();             // B2(i+1)
+          } else {
+            if (i + 2 < nsteps) consume();   // staged data of step i+2
+            barrier_lds();             // B1(i+1): P(i), alpha(i) and step i's bf16 slot are free
+            publish(pk, alpha);
+            if (i + 2 < nsteps) dequant(comp_slot);
+            barrier_lds();             // B2(i+1)
+          }
         }
         comp_slot = cs_next;
         zcur = znext;
@@ -708,29 +836,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
+template <bool kFp8>
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   // the LDS opt-in is per device; remember it per device id
   static thread_local int configured = -1;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (configured != dev) {
-    e = hipFuncSetAttribute((const void*)decode_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    e = hipFuncSetAttribute((const void*)decode_kernel<kFp8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            Lds<kFp8>::kBytes);
     if (e != hipSuccess) return e;
     configured = dev;
   }
-  hipLaunchKernelGGL(decode_kernel<false>, dim3(a.workers), dim3(kThreads), kLdsBytes, stream,
+  hipLaunchKernelGGL(decode_kernel<kFp8>, dim3(a.workers), dim3(kThreads), Lds<kFp8>::kBytes, stream,
                      reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const char*>(a.kv), a.kv_scales,
                      a.block_table, a.seqlens, a.plan, a.ws, a.out, a.lse, scalars_of(a));
   return hipGetLastError();
 }
 
-hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream) {
-  (void)a; (void)stream;
-  return hipErrorNotSupported;
-}
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch_decode<false>(a, stream); }
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream) { return launch_decode<true>(a, stream); }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
   const int max_split = a.workers;   // split items <= active workers - 1

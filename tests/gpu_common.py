@@ -1,4 +1,6 @@
 """Helpers shared by the GPU tests: upload a workload, run the library, compare with the oracle."""
+import os
+
 import numpy as np
 import torch
 
@@ -6,11 +8,13 @@ import mla_latent_space_amd as mla
 
 # Tolerances on out (float32 [b, s, h, 512]) and lse. bf16 cache: rel L2 <= 5e-3, max abs
 # <= 2e-2, |d lse| <= 1e-3. fp8 cache: compared with the oracle on the same dequantised
-# values, rel L2 <= 3e-2; every e4m3 code is exact in bf16 and the scales are applied in
-# fp32, so the remaining error sources are those of the bf16 path and its max abs / lse
-# bounds are kept.
+# values, rel L2 <= 3e-2 (the stated fp8 bound). Its max abs and lse bounds follow from
+# the arithmetic: the kernel dequantises each value once into bf16 (relative error
+# <= 2^-9), which moves a score by at most softmax_scale * 2^-9 * sum_c |q_c z_c| (about
+# 5e-2 worst case and 3e-3 typical for these N(0,1) draws); lse moves by no more than the
+# largest score error, so fp8 lse is held to 2e-2 and max abs keeps the bf16 bound.
 BF16_TOL = dict(rel_l2=5e-3, max_abs=2e-2, lse=1e-3)
-FP8_TOL = dict(rel_l2=3e-2, max_abs=2e-2, lse=1e-3)
+FP8_TOL = dict(rel_l2=3e-2, max_abs=2e-2, lse=2e-2)
 
 
 class Dev:
@@ -52,5 +56,9 @@ def compare(out, lse, ref_out, ref_lse, tol, what=""):
     mabs = float(np.max(np.abs(out - ref_out))) if out.size else 0.0
     dl = float(np.max(np.abs(lse[~ninf] - ref_lse[~ninf]))) if (~ninf).any() else 0.0
     msg = f"{what}: rel_l2={rel:.3e} max_abs={mabs:.3e} max_dlse={dl:.3e}"
+    log = os.environ.get("MLA_PARITY_LOG")
+    if log:   # margins of passing cases, for the record
+        with open(log, "a") as f:
+            f.write(msg + "\n")
     assert rel <= tol["rel_l2"] and mabs <= tol["max_abs"] and dl <= tol["lse"], msg
     return rel, mabs, dl

@@ -202,3 +202,44 @@ def test_jagged_full_size_sampled():
     pick = [int(np.argmax(lens)), int(np.argmin(lens)), int(np.argsort(lens)[len(lens) // 2])]
     _say("jagged full size, seqs", pick, "lens", [int(lens[i]) for i in pick])
     _check_sampled(w, pick)
+
+
+# ----------------------------------------------------------------------------- fp8 cache
+
+@pytest.mark.parametrize("W", [1, 5, 256])
+def test_fp8_ragged_any_worker_count(W):
+    """fp8 cache (codes + per-128-channel scales + bf16 rope): lengths that end mid-page and
+    mid-step, a one-token sequence, many pages; poisoned tails and spare pages."""
+    w = wl.make_workload("fp8-ragged", batch=6, s_q=1, heads=128, seqlens=[1, 31, 63, 64, 65, 1000],
+                         kv_dtype="fp8", seed=31)
+    _say("fp8 ragged W", W)
+    _check_full(w, num_workers=W, what=f"fp8 ragged W={W}")
+
+
+@pytest.mark.parametrize("heads,s_q,causal", [(16, 1, False), (64, 4, True), (128, 16, True)])
+def test_fp8_heads_and_query_tokens(heads, s_q, causal):
+    w = wl.make_workload("fp8-heads", batch=3, s_q=s_q, heads=heads, seqlens=[s_q, 130, 517], kv_dtype="fp8",
+                         causal=causal, seed=32 + heads + s_q)
+    _say("fp8 heads", heads, "s_q", s_q, "causal", causal)
+    _check_full(w, num_workers=11, what=f"fp8 h={heads} s={s_q} causal={causal}")
+
+
+def test_fp8_empty_and_bitwise_repeat():
+    w = wl.make_workload("fp8-empty", batch=3, s_q=2, heads=32, seqlens=[0, 1, 300], kv_dtype="fp8", causal=True,
+                         seed=33)
+    _say("fp8 empty + repeat")
+    d = Dev(w)
+    plan = d.plan(4)
+    o1, l1 = d.run(plan=plan)
+    o2, l2 = d.run(plan=plan)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ro, rl = _oracle_all(w)
+    compare(o1.cpu().numpy(), l1.cpu().numpy(), ro, rl, FP8_TOL, "fp8 empty")
+    assert (o1[0] == 0).all()
+
+
+def test_fp8_full_size_sampled():
+    """64 sequences of 32,768 tokens, fp8 cache; every row of three sequences."""
+    w = wl.make_config("fp8")
+    _say("fp8 full size")
+    _check_sampled(w, [0, 29, 63])
