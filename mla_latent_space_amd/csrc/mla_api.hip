@@ -58,7 +58,7 @@ size_t workspace_bytes_of(int32_t batch, int32_t s_q, int32_t heads, int32_t wor
   int64_t slots = 2 * ((int64_t)workers - 1);
   if (slots > 2 * n * workers) slots = 2 * n * workers;
   if (slots < 0) slots = 0;
-  return (size_t)slots * (size_t)mla::kSlotFloats * sizeof(float);
+  return (size_t)slots * (size_t)mla::kSlotBytes;
 }
 
 }  // namespace

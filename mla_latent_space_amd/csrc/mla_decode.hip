@@ -717,27 +717,48 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
         stat_l[mrow] = l_run;
       }
       barrier_lds();
+      if (split) {
+        // partial: bf16, each store one 512-B run in register order (see combine_kernel)
+        char* part = reinterpret_cast<char*>(ws) + (int64_t)slot * kSlotBytes;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int row = 32 * nt + (l & 31);
-        const int grow = kRowsPerTile * f_tile + row;
-        if (grow >= rows_total) continue;
-        const float lsum = stat_l[row];
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        const int jt = grow / a.heads, hd = grow - jt * a.heads;
-        float* dst = split ? (ws + (int64_t)slot * kSlotFloats + (int64_t)row * kLat)
-                           : (out_ptr + ((int64_t)(f_seq * a.s_q + jt) * a.heads + hd) * kLat);
+        for (int nt = 0; nt < 4; ++nt) {
+          const float lsum = stat_l[32 * nt + (l & 31)];
+          const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+          for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int c = 64 * wave + 32 * mt + 8 * g + 4 * (l >> 5);
-            f32x4 v;
-            v[0] = oacc[mt][nt][4 * g + 0] * inv;
-            v[1] = oacc[mt][nt][4 * g + 1] * inv;
-            v[2] = oacc[mt][nt][4 * g + 2] * inv;
-            v[3] = oacc[mt][nt][4 * g + 3] * inv;
-            *reinterpret_cast<f32x4*>(dst + c) = v;
+            for (int g = 0; g < 4; ++g) {
+              bf16x4 v;
+              v[0] = (__bf16)(oacc[mt][nt][4 * g + 0] * inv);
+              v[1] = (__bf16)(oacc[mt][nt][4 * g + 1] * inv);
+              v[2] = (__bf16)(oacc[mt][nt][4 * g + 2] * inv);
+              v[3] = (__bf16)(oacc[mt][nt][4 * g + 3] * inv);
+              const int frag = (((wave * 4 + nt) * 2 + mt) * 4 + g) * 64 + l;
+              *reinterpret_cast<bf16x4*>(part + 8 * (int64_t)frag) = v;
+            }
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int row = 32 * nt + (l & 31);
+          const int grow = kRowsPerTile * f_tile + row;
+          if (grow >= rows_total) continue;
+          const float lsum = stat_l[row];
+          const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+          const int jt = grow / a.heads, hd = grow - jt * a.heads;
+          float* dst = out_ptr + ((int64_t)(f_seq * a.s_q + jt) * a.heads + hd) * kLat;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int c = 64 * wave + 32 * mt + 8 * g + 4 * (l >> 5);
+              f32x4 v;
+              v[0] = oacc[mt][nt][4 * g + 0] * inv;
+              v[1] = oacc[mt][nt][4 * g + 1] * inv;
+              v[2] = oacc[mt][nt][4 * g + 2] * inv;
+              v[3] = oacc[mt][nt][4 * g + 3] * inv;
+              *reinterpret_cast<f32x4*>(dst + c) = v;
+            }
           }
         }
       }
@@ -746,7 +767,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
         const float m = (m_run == -INFINITY) ? 0.f : m_run;
         const float lse_v = l_run > 0.f ? (m + __log2f(l_run)) * 0.6931471805599453f : -INFINITY;
         const int jt = grow / a.heads, hd = grow - jt * a.heads;
-        if (split) ws[(int64_t)slot * kSlotFloats + (int64_t)kRowsPerTile * kLat + mrow] = lse_v;
+        if (split) reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (int64_t)slot * kSlotBytes + kSlotPartBytes)[mrow] = lse_v;
         else lse_ptr[(int64_t)(f_seq * a.s_q + jt) * a.heads + hd] = lse_v;
       }
       barrier_lds();
@@ -758,16 +779,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
 }
 
 // Merge the partials of split items: lse = log sum_k e^{lse_k}, out = sum_k e^{lse_k - lse} O_k
-// (max-shifted; parts with lse = -inf carry no weight). One block per (split item, 16 rows):
-// the per-(row, split) weights are staged in LDS, then every thread streams float4 columns
-// of 8 rows with all 8 loads of a split in flight.
-constexpr int kCombRows = 16;
+// (max-shifted; parts with lse = -inf carry no weight). One block per (split item, 32-row
+// group nt). A partial is stored in the decode kernel's register order: value
+// (row 32nt + (lane & 31), channel 64w + 32mt + 8g + 4(lane >> 5) + e) of a slot sits at
+// bf16 index 4 * ((((w * 4 + nt) * 2 + mt) * 4 + g) * 64 + lane) + e, so a block reads each
+// part as 8 contiguous 4-KiB runs. The merged rows go through LDS to leave as whole rows.
 constexpr int kCombMaxSplits = 256;
+constexpr int kCombThreads = 256;
 
-__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ plan,
-                                                      const float* __restrict__ ws, float* __restrict__ out,
-                                                      float* __restrict__ lse, int s_q, int heads) {
-  __shared__ float wts[kCombRows][kCombMaxSplits];
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(const int32_t* __restrict__ plan,
+                                                               const char* __restrict__ ws, float* __restrict__ out,
+                                                               float* __restrict__ lse, int s_q, int heads) {
+  __shared__ float wts[32][kCombMaxSplits];
+  __shared__ float tile_out[32][kLat + 4];   // +4: rows start on different banks
+  __shared__ float row_m[32], row_t[32];
   if (plan[kHMagic] != kPlanMagic) return;
   const int n_split = plan[kHSplitItems];
   const int n_items = plan[kHItems];
@@ -776,63 +801,92 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const int32_t* it = plan + plan_items_off() + kItemWords * k;
   const int seq = it[kISeq], tile = it[kITile], ns_all = it[kINsplits], slot0 = it[kISlot];
   const int rows_total = s_q * heads;
-  const int r0 = blockIdx.y * kCombRows;
+  const int nt = blockIdx.y;
+  if (kRowsPerTile * tile + 32 * nt >= rows_total) return;
   const int tid = threadIdx.x;
-  const int64_t lse_off = (int64_t)kRowsPerTile * kLat;
-  // splits are merged in chunks of kCombMaxSplits (one chunk in practice); the running
-  // (max, sum, acc) of earlier chunks is rescaled like the online softmax
-  const int c4 = (tid & 127) * 4;
-  const int rsub = tid >> 7;
-  f32x4 acc[8];
-  float tot[8];
+  // this thread's 16 fragments: p = tid + 256 j -> (w, mt, g, lane)
+  f32x4 acc[16];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { acc[j] = f32x4{0.f, 0.f, 0.f, 0.f}; tot[j] = 0.f; }
-  float mrow[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) mrow[j] = -INFINITY;
+  for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_old = -INFINITY;   // per row, kept by threads tid < 32
+  float t_old = 0.f;
   for (int s0 = 0; s0 < ns_all; s0 += kCombMaxSplits) {
     const int ns = ns_all - s0 < kCombMaxSplits ? ns_all - s0 : kCombMaxSplits;
     __syncthreads();
-    for (int idx = tid; idx < kCombRows * ns; idx += 256) {
+    for (int idx = tid; idx < 32 * ns; idx += kCombThreads) {
       const int r = idx / ns, sp = idx - r * ns;
-      wts[r][sp] = ws[(int64_t)(slot0 + s0 + sp) * kSlotFloats + lse_off + r0 + r];
+      wts[r][sp] = reinterpret_cast<const float*>(ws + (int64_t)(slot0 + s0 + sp) * kSlotBytes + kSlotPartBytes)[32 * nt + r];
+    }
+    __syncthreads();
+    // per row: new running max, weights relative to it, rescale of the earlier chunks
+    if (tid < 32) {
+      float m = m_old;
+      for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, wts[tid][sp]);
+      const float safe = m == -INFINITY ? 0.f : m;
+      const float resc = m_old == -INFINITY ? 0.f : __expf(m_old - safe);
+      float tot = t_old * resc;
+      for (int sp = 0; sp < ns; ++sp) {
+        const float l = wts[tid][sp];
+        const float wgt = l == -INFINITY ? 0.f : __expf(l - safe);
+        wts[tid][sp] = wgt;
+        tot += wgt;
+      }
+      m_old = m;
+      t_old = tot;
+      row_m[tid] = resc;   // (rescale of the accumulators, read below)
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = rsub + 2 * j;
-      float m = mrow[j];
-      for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, wts[r][sp]);
-      const float safe = m == -INFINITY ? 0.f : m;
-      const float resc = mrow[j] == -INFINITY ? 0.f : __expf(mrow[j] - safe);
-      acc[j] *= resc;
-      tot[j] *= resc;
-      mrow[j] = m;
-    }
+    for (int j = 0; j < 16; ++j) acc[j] *= row_m[(tid + 256 * j) & 31];
     for (int sp = 0; sp < ns; ++sp) {
-      const float* base = ws + (int64_t)(slot0 + s0 + sp) * kSlotFloats + c4;
-      f32x4 v[8];
+      const __bf16* part = reinterpret_cast<const __bf16*>(ws + (int64_t)(slot0 + s0 + sp) * kSlotBytes);
+      bf16x4 v[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const f32x4*>(base + (int64_t)(r0 + rsub + 2 * j) * kLat);
+      for (int j = 0; j < 16; ++j) {
+        const int p = tid + 256 * j;
+        const int lane = p & 63, g = (p >> 6) & 3, mt = (p >> 8) & 1, w = p >> 9;
+        const int frag = (((w * 4 + nt) * 2 + mt) * 4 + g) * 64 + lane;
+        v[j] = *reinterpret_cast<const bf16x4*>(part + 4 * (int64_t)frag);
+      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float l = wts[rsub + 2 * j][sp];
-        const float wgt = l == -INFINITY ? 0.f : __expf(l - (mrow[j] == -INFINITY ? 0.f : mrow[j]));
-        tot[j] += wgt;
-        if (wgt != 0.f) acc[j] += wgt * v[j];
+      for (int j = 0; j < 16; ++j) {
+        const float wgt = wts[(tid + 256 * j) & 31][sp];
+        acc[j][0] += wgt * (float)v[j][0];
+        acc[j][1] += wgt * (float)v[j][1];
+        acc[j][2] += wgt * (float)v[j][2];
+        acc[j][3] += wgt * (float)v[j][3];
       }
     }
   }
+  if (tid < 32) {
+    row_t[tid] = t_old;
+    row_m[tid] = m_old;
+  }
+  __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = r0 + rsub + 2 * j;
-    const int grow = kRowsPerTile * tile + r;
+  for (int j = 0; j < 16; ++j) {
+    const int p = tid + 256 * j;
+    const int lane = p & 63, g = (p >> 6) & 3, mt = (p >> 8) & 1, w = p >> 9;
+    const int r = lane & 31, c = 64 * w + 32 * mt + 8 * g + 4 * (lane >> 5);
+    const float t = row_t[r];
+    const float inv = t > 0.f ? 1.f / t : 0.f;
+    *reinterpret_cast<f32x4*>(&tile_out[r][c]) = acc[j] * inv;
+  }
+  __syncthreads();
+  // whole rows out: 32 rows x 128 float4
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int idx = tid + 256 * j;
+    const int r = idx >> 7, c4 = (idx & 127) * 4;
+    const int grow = kRowsPerTile * tile + 32 * nt + r;
     if (grow >= rows_total) continue;
     const int jt = grow / heads, hd = grow - jt * heads;
     const int64_t orow = (int64_t)(seq * s_q + jt) * heads + hd;
-    const float inv = tot[j] > 0.f ? 1.f / tot[j] : 0.f;
-    *reinterpret_cast<f32x4*>(out + orow * kLat + c4) = acc[j] * inv;
-    if (c4 == 0) lse[orow] = tot[j] > 0.f ? mrow[j] + __logf(tot[j]) : -INFINITY;
+    *reinterpret_cast<f32x4*>(out + orow * kLat + c4) = *reinterpret_cast<const f32x4*>(&tile_out[r][c4]);
+    if (c4 == 0) {
+      const float t = row_t[r];
+      lse[orow] = t > 0.f ? row_m[r] + __logf(t) : -INFINITY;
+    }
   }
 }
 
@@ -863,8 +917,8 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream) { return l
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
   const int max_split = a.workers;   // split items <= active workers - 1
-  hipLaunchKernelGGL(combine_kernel, dim3(max_split, kRowsPerTile / kCombRows), dim3(256), 0, stream, a.plan, a.ws,
-                     a.out, a.lse, a.s_q, a.heads);
+  hipLaunchKernelGGL(combine_kernel, dim3(max_split, kRowsPerTile / 32), dim3(kCombThreads), 0, stream, a.plan,
+                     reinterpret_cast<const char*>(a.ws), a.out, a.lse, a.s_q, a.heads);
   return hipGetLastError();
 }
 

@@ -44,8 +44,11 @@ __host__ __device__ inline int tiles_per_seq(int s_q, int heads) {
   return (s_q * heads + kRowsPerTile - 1) / kRowsPerTile;
 }
 
-// Workspace: per partial slot, 128 rows x 512 fp32 (normalised partial out) + 128 fp32 lse.
-constexpr int64_t kSlotFloats = (int64_t)kRowsPerTile * kLat + kRowsPerTile;
+// Workspace: per partial slot (one split part of a 128-row item), the normalised partial
+// out as bf16 in the value MFMAs' register order (128 x 512 values, see the decode kernel's
+// finalize), then 128 fp32 lse.
+constexpr int64_t kSlotPartBytes = (int64_t)kRowsPerTile * kLat * 2;
+constexpr int64_t kSlotBytes = kSlotPartBytes + (int64_t)kRowsPerTile * 4;
 
 hipError_t launch_plan(const int32_t* seqlens, int batch, int s_q, int heads, int causal, int workers,
                        int32_t* plan, hipStream_t stream);
