@@ -344,7 +344,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
   char __attribute__((address_space(3)))* lds = (char __attribute__((address_space(3)))*)smem_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int worker = blockIdx.x;
+  // Work-groups are dealt to the 8 XCDs round-robin (block b -> XCD b % 8). Plan workers
+  // are numbered so that consecutive ones (the parts of one split item, which all load the
+  // item's queries) share an XCD and its L2: worker = (blocks on lower XCDs) + b / 8.
+  const int worker = [] {
+    const int b = blockIdx.x, n = gridDim.x, x = b & 7;
+    int before = 0;
+    for (int y = 0; y < x; ++y) before += (n - y + 7) >> 3;
+    return before + (b >> 3);
+  }();
   if (plan[kHMagic] != kPlanMagic || plan[kHWorkers] != (int)gridDim.x || plan[kHBatch] != a.batch ||
       plan[kHSq] != a.s_q || plan[kHHeads] != a.heads || plan[kHCausal] != a.causal)
     return;
@@ -569,6 +577,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
     };
     auto values_and_softmax = [&](const char __attribute__((address_space(3)))* zb, const f32x4* sacc, int hh_next,
                                   bool live, bf16x4* pk, float* alpha_out) {
+      // the value MFMAs get issue priority over the score tiles of the SIMD's other wave
+      __builtin_amdgcn_s_setprio(1);
       // 8 (k-step q, row tile nt) pairs, 2 MFMAs each; P operands one pair ahead, the
       // transposed Z^T operands of k-step 1 read during k-step 0
       const char __attribute__((address_space(3)))* prow = pbuf + (lane & 31) * kPRowBytes + 16 * (lane >> 5);
@@ -607,6 +617,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     // wait until this wave's DMA of the oldest unconsumed step has landed (younger
     // steps stay in flight)
