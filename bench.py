@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="KV copies to cycle through (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB --steps times (the reference "
+                         "kernel for scaling HBM byte counters), print its size and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build measures the single-GPU decode path "
@@ -117,6 +120,15 @@ def main():
     from mla_latent_space_amd import workloads as wl
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "calls": args.steps}), flush=True)
+        return
     w = wl.make_config(args.workload)
     dev = torch.device("cuda", 0)
     q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
