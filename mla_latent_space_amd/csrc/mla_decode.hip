@@ -298,6 +298,7 @@ __device__ __forceinline__ void dequant_step(const char __attribute__((address_s
 }
 
 constexpr int kQkAhead = 4;   // score-operand reads in flight ahead of the MFMA consuming them
+constexpr int kPvAhead = 2;   // P-operand reads in flight ahead of the value MFMAs
 
 // LDS byte offset (inside a slot) of score tile t: token tile t%2, 32-channel k-step t/2
 __device__ __forceinline__ int qk_off(const int* qk_b, int t) {
@@ -591,12 +592,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(
         const bf16x4 hi = lds_tr16(zb + pv_base[1][mt]);
         av[0][mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      bf16x8 bnext = lds_b128(prow);
+      // P operands kPvAhead pairs ahead of their MFMAs
+      bf16x8 pring[kPvAhead];
+#pragma unroll
+      for (int j = 0; j < kPvAhead; ++j) pring[j] = lds_b128(prow + (j & 3) * 32 * kPRowBytes + 32 * (j >> 2));
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int q = j >> 2, nt = j & 3;
-        const bf16x8 bp = bnext;
-        if (j + 1 < 8) bnext = lds_b128(prow + ((j + 1) & 3) * 32 * kPRowBytes + 32 * ((j + 1) >> 2));
+        const bf16x8 bp = pring[j % kPvAhead];
+        if (j + kPvAhead < 8)
+          pring[j % kPvAhead] = lds_b128(prow + ((j + kPvAhead) & 3) * 32 * kPRowBytes + 32 * ((j + kPvAhead) >> 2));
         if (j == 1) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
