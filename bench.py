@@ -74,8 +74,9 @@ def traffic_from_profile(kernel_srcs, key):
 
 
 def cpu_baseline(w, budget_s: float):
-    """The oracle (as is) on the first sequences of the workload until ~budget_s of host time,
-    extrapolated to the whole batch."""
+    """The oracle (as is) over the workload's sequences, one at a time, until ~budget_s of
+    host time (whole passes over the batch are repeated if one pass is shorter), scaled to
+    one call over the whole batch."""
     import numpy as np
     from oracle import mla as om
     try:
@@ -83,17 +84,21 @@ def cpu_baseline(w, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    done = 0
+    lens = w.seqlens.astype(np.int64)
+    total = float(np.sum(lens))
+    done_tokens = 0.0
+    seqs = 0
     t0 = time.perf_counter()
-    while done < w.batch and (time.perf_counter() - t0) < budget_s:
-        om.decode_latent(w.q, w.kv, w.kv_scales, w.kv_dtype, w.block_table, w.seqlens, w.scale, w.causal, [done])
-        done += 1
+    while (time.perf_counter() - t0) < budget_s:
+        i = seqs % w.batch
+        om.decode_latent(w.q, w.kv, w.kv_scales, w.kv_dtype, w.block_table, w.seqlens, w.scale, w.causal, [i])
+        done_tokens += float(lens[i])
+        seqs += 1
     el = time.perf_counter() - t0
-    frac = float(np.sum(w.seqlens[:done].astype(np.int64))) / float(np.sum(w.seqlens.astype(np.int64)))
-    us = el / frac * 1e6
-    return {"value": round(us, 1), "unit": "µs/call", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 oracle on {done} of {w.batch} sequences ({frac * 100:.1f}% of the tokens) of the "
-                      f"{w.name} workload, {el:.1f} s, scaled to the whole batch"}
+    calls = done_tokens / total
+    return {"value": round(el / calls * 1e6, 1), "unit": "µs/call", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle over {seqs} sequences of the {w.name} workload ({calls:.2f} x its "
+                      f"{w.batch} sequences by cached tokens) in {el:.1f} s of host time, scaled to one call"}
 
 
 def main():

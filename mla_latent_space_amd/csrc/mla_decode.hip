@@ -8,24 +8,31 @@
 // decode is bound by HBM, so the design streams each cached token row from HBM exactly
 // once per 128-row tile and keeps the matrix cores busy underneath.
 //
-// Work-group = 4 waves = one persistent worker of the split plan, one per compute unit.
-//  * LDS ring of 4 steps x 32 tokens x 1152 B, filled by LDS-DMA buffer loads (16 B per
-//    lane, coalesced). The buffer descriptor's record count stops at the last visible
-//    token, so masked tail slots arrive as zeros (poisoned slots never reach the MFMAs).
-//    Rows are XOR-swizzled in 16-B chunks (chunk ^= (token >> 1) & 7) so that both LDS
-//    read patterns below are free of bank conflicts.
-//  * Scores: wave w owns query rows 32w..32w+31 of the tile and computes S^T = Z Q^T with
-//    v_mfma_f32_32x32x16_bf16: A = 32 tokens x 16 channels read from LDS (ds_read_b128),
-//    B = Q^T held in 144 VGPRs for the whole sequence segment.
-//  * Online softmax in the S^T layout: each lane owns one query row and 16 of the 32
-//    tokens, so row max / row sum are lane-local plus one permlane32 swap. The running
+// Work-group = 8 waves (two per SIMD) = one persistent worker of the split plan, one per
+// compute unit; it walks its contiguous run of (item, page) pairs in 32-token steps.
+//  * LDS ring of 4 steps x 32 tokens x 1152 B, filled by LDS-DMA buffer loads
+//    (buffer_load_dwordx4 ... lds: 1 KiB per wave instruction, 16 B per lane, coalesced).
+//    The buffer descriptor's record count stops at the last visible token, so masked tail
+//    rows arrive as zeros (poisoned slots never reach the MFMAs). Rows are XOR-swizzled
+//    in 16-B chunks (chunk ^= (token >> 1) & 7) so that both LDS read patterns below are
+//    free of bank conflicts. Each compute region issues one step, its DMA instructions
+//    interleaved with the score MFMAs; each wave waits (vmcnt) only for its own loads.
+//  * Scores: wave w owns query rows 16w..16w+15 of the 128-row tile and computes
+//    S^T = Z Q^T with v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 channels read from LDS
+//    (ds_read_b128), B = Q^T held in 72 VGPRs for the whole segment.
+//  * Online softmax in the S^T layout: each lane owns one query row and 8 of the 32
+//    tokens, so row max / row sum are lane-local plus permlane16/32 swaps. The running
 //    max is only moved when it grows by more than 2^8 (lazy rescale), so the accumulator
-//    is rarely rescaled.
-//  * P (bf16) goes through LDS already in the MFMA B-operand layout; value products are
-//    split by channels: wave w owns O^T[128w .. 128w+127][all 128 rows] (256 acc regs),
-//    A = Z^T via ds_read_b64_tr_b16 (transposing LDS read), B = P^T from LDS.
-//  * Finalize writes out/lse directly, or a normalised partial + lse into the workspace
-//    for items the plan split; the combine kernel merges those by log-sum-exp.
+//    is rarely rescaled; the softmax of step i+1 is interleaved with the value MFMAs of
+//    step i.
+//  * P (bf16) goes through LDS in the MFMA B-operand layout; value products are split
+//    by channels: wave w owns O^T[64w .. 64w+63][all 128 rows] (128 accumulator VGPRs),
+//    A = Z^T via ds_read_b64_tr_b16 (transposing LDS read), B = P^T from LDS, with
+//    v_mfma_f32_32x32x16_bf16.
+//  * Finalize writes out/lse directly, or a normalised bf16 partial + lse into the
+//    workspace for items the plan split; the combine kernel merges those by log-sum-exp.
+//  * fp8 cache: each half page is staged as loaded (codes, rope, scales) and dequantised
+//    once per step into a bf16 slot of the same layout, then the same code runs.
 #include "mla_internal.h"
 
 namespace mla {
@@ -216,12 +223,16 @@ __device__ __forceinline__ StepRsrc cursor_rsrc(const LoadCursor& c, const Scala
 // Per-lane source offsets of this wave's LDS-DMA instructions. Instruction i (1 KiB,
 // 64 lanes x 16 B, lane-linear in LDS) is issued by wave i % 8; LDS chunk position
 // p = 72u + pc holds logical chunk ch = pc ^ swz(u) of token u.
+// Only full-rate 24-bit multiplies: with x = p * 1821, u = floor(p / 72) = x >> 17 and
+// p mod 72 = ((x mod 2^17) * 72) >> 17, exactly for every p < 2304 (a step's 36 x 64 chunk
+// positions; both products stay below 2^24).
 __device__ __forceinline__ uint32_t dma_voff(int wave, int n, int lane) {
-  const int i = wave + 8 * n;
-  const int p = 64 * i + lane;
-  const int u = p / 72, pc = p - 72 * u;
-  const int ch = (pc & ~7) | ((pc & 7) ^ swz(u));
-  return (uint32_t)(u * kRowBytes + 16 * ch);
+  const uint32_t p = 64u * (uint32_t)(wave + 8 * n) + (uint32_t)lane;
+  const uint32_t x = __umul24(p, 1821u);
+  const uint32_t u = x >> 17;
+  const uint32_t pc = __umul24(x & 0x1FFFFu, 72u) >> 17;
+  const uint32_t ch = (pc & ~7u) | ((pc & 7u) ^ (uint32_t)swz((int)u));
+  return __umul24(u, (uint32_t)kRowBytes) + 16u * ch;
 }
 
 // One of this wave's LDS-DMA instructions of a step: instruction i = wave + 8n. The per-lane
