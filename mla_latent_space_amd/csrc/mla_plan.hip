@@ -13,7 +13,8 @@
 namespace mla {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 1024;         // block size for batches of more than 256 items
+constexpr int kThreadsSmall = 256;     // ... and up to 256 items (cheaper barriers)
 constexpr int kWaves = kThreads / 64;
 
 __device__ inline void item_shape(const int32_t* seqlens, int idx, int tiles, int s_q, int heads, int causal,
@@ -37,7 +38,7 @@ __device__ inline void item_shape(const int32_t* seqlens, int idx, int tiles, in
 }
 
 // Exclusive scan over the block: each thread contributes `x`, returns its exclusive prefix,
-// `total` gets the block sum. `scratch` holds >= kWaves ints.
+// `total` gets the block sum. `scratch` holds >= blockDim.x / 64 ints.
 __device__ inline int block_exclusive_scan(int x, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = x;
@@ -49,7 +50,8 @@ __device__ inline int block_exclusive_scan(int x, int* scratch, int* total) {
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
   int wave_off = 0, tot = 0;
-  for (int w = 0; w < kWaves; ++w) {
+  const int nwaves = blockDim.x >> 6;
+  for (int w = 0; w < nwaves; ++w) {
     const int s = scratch[w];
     wave_off += (w < wave) ? s : 0;
     tot += s;
@@ -74,21 +76,33 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
   int* scratch = tile_tot + 256;                                // [kWaves]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nthreads = blockDim.x;
   const int tiles = tiles_per_seq(s_q, heads);
   const int n = batch * tiles;
 
   // keys: (0xFFFF - pages) in the high half sorts longest first; the item index in the
   // low half is already ascending, and the LSD passes are stable.
-  for (int i = tid; i < n; i += kThreads) {
+  // (all page counts equal -- e.g. one length for the whole batch -- means the item order
+  // is already sorted)
+  int first_pages;
+  {
+    int sq0, tl0, vis0;
+    item_shape(seqlens, 0, tiles, s_q, heads, causal, &sq0, &tl0, &vis0, &first_pages);
+  }
+  bool same = true;
+  for (int i = tid; i < n; i += nthreads) {
     int sq, tl, vis, pages;
     item_shape(seqlens, i, tiles, s_q, heads, causal, &sq, &tl, &vis, &pages);
     keys_a[i] = ((uint32_t)(0xFFFF - pages) << 16) | (uint32_t)i;
+    same = same && pages == first_pages;
   }
-  __syncthreads();
+  const bool uniform = __syncthreads_and(same);
 
   uint32_t* src = keys_a;
   uint32_t* dst = keys_b;
-  if (n <= kThreads) {
+  if (uniform) {
+    // nothing to sort
+  } else if (n <= nthreads) {
     // Small batches: the packed keys are unique, so each item's position is the number of
     // smaller keys (a rank sort; same order as the radix sort below).
     const int n4 = (n + 3) & ~3;
@@ -110,9 +124,9 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     // ordered through per-digit counters.
     for (int shift = 16; shift < 32; shift += 8) {
       if (tid < 256) digit_base[tid] = 0;
-      for (int i = tid; i < kWaves * 256; i += kThreads) wave_cnt[i] = 0;
+      for (int i = tid; i < kWaves * 256; i += nthreads) wave_cnt[i] = 0;
       __syncthreads();
-      for (int i = tid; i < n; i += kThreads) atomicAdd(&digit_base[(src[i] >> shift) & 255], 1);
+      for (int i = tid; i < n; i += nthreads) atomicAdd(&digit_base[(src[i] >> shift) & 255], 1);
       __syncthreads();
       {
         int tot_unused = 0;
@@ -121,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
         if (tid < 256) digit_base[tid] = excl;
         __syncthreads();
       }
-      for (int t0 = 0; t0 < n; t0 += kThreads) {
+      for (int t0 = 0; t0 < n; t0 += nthreads) {
         const int i = t0 + tid;
         const bool valid = i < n;
         const uint32_t v = valid ? src[i] : 0u;
@@ -137,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
         __syncthreads();
         if (tid < 256) {
           int run = 0;
-          for (int w = 0; w < kWaves; ++w) {
+          for (int w = 0; w < (nthreads >> 6); ++w) {
             const int c = wave_cnt[w * 256 + tid];
             wave_cnt[w * 256 + tid] = run;
             run += c;
@@ -149,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
         __syncthreads();
         if (tid < 256) {
           digit_base[tid] += tile_tot[tid];
-          for (int w = 0; w < kWaves; ++w) wave_cnt[w * 256 + tid] = 0;
+          for (int w = 0; w < (nthreads >> 6); ++w) wave_cnt[w * 256 + tid] = 0;
         }
         __syncthreads();
       }
@@ -158,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
   }
   // src holds the sorted keys; dst becomes the cost prefix C_k.
   int* cost = reinterpret_cast<int*>(dst);
-  const int per = (n + kThreads - 1) / kThreads;
+  const int per = (n + nthreads - 1) / nthreads;
   const int lo = tid * per;
   const int hi = lo + per < n ? lo + per : n;
   int local = 0;
@@ -208,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
   }
   // workers: start(w) = (item holding position floor(w C / Weff), page offset)
   int32_t* workers = plan + plan_workers_off(n);
-  for (int w = tid; w < W; w += kThreads) {
+  for (int w = tid; w < W; w += nthreads) {
     int sk[2], sp[2];
     for (int e = 0; e < 2; ++e) {
       const int64_t ww = w + e;
@@ -262,7 +276,9 @@ hipError_t launch_plan(const int32_t* seqlens, int batch, int s_q, int heads, in
     if (e != hipSuccess) return e;
     configured = dev;
   }
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), kPlanLds, stream, seqlens, batch, s_q, heads, causal,
+  const int n_items = batch * tiles_per_seq(s_q, heads);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(n_items <= kThreadsSmall ? kThreadsSmall : kThreads), kPlanLds, stream,
+                     seqlens, batch, s_q, heads, causal,
                      workers, plan);
   return hipGetLastError();
 }

@@ -66,6 +66,9 @@ PLAN_CASES = [
     dict(seqlens=[256, 256], s_q=1, h=16, causal=False, W=256),
     dict(seqlens="jagged", s_q=1, h=128, causal=False, W=256),
     dict(seqlens="random3000", s_q=2, h=64, causal=True, W=1000),
+    dict(seqlens=[1000] * 2000, s_q=1, h=128, causal=False, W=256),    # one length, radix-size batch
+    dict(seqlens=[500] * 300, s_q=1, h=64, causal=False, W=97),        # one length, 257..1024 items
+    dict(seqlens=[700, 700, 64, 700] * 70, s_q=1, h=128, causal=False, W=256),   # 257..1024, mixed
 ]
 
 
