@@ -1,0 +1,714 @@
+// Latent-space MLA decode over a bf16 cache: one persistent work-group of four waves (one per
+// SIMD) per compute unit, each wave owning 32 query rows of the 128-row tile end to end.
+//
+// Page "Mla Analysis", section "Absorption Trick (FlashMLA)": scores are Qz . Z^T with the
+// absorbed 576-wide queries and the value is the latent row itself, so one pass over the
+// paged latent cache gives O_latent = softmax(scale Qz Z^T) Z[:, :512] and a log-sum-exp per
+// (token, head). Section "Cost Models": at s=1 this is about 228 FLOP per byte, under the
+// MI355X bf16 ridge, so the kernel streams every cached row from HBM once per 128-row tile
+// and keeps the matrix cores busy underneath.
+//
+// Per 32-token step, per wave (rows 32w .. 32w+31):
+//  * Scores S^T[32 tokens x 32 rows] = Z Q^T: 36 v_mfma_f32_32x32x16_bf16 over the 576
+//    channels; A = Z rows from LDS (ds_read_b128), B = Q^T held in 144 VGPRs.
+//  * The 32x32 accumulator layout (lane: row l%32, tokens 8j + 4(l/32) + v) is, after the
+//    bf16 rounding, exactly an MFMA operand of P[32 rows x 16 tokens] when the 16 k slots
+//    of k-step q are taken as tokens 16q + 8(i/4) + 4(l/32) + i%4. So P never leaves the
+//    registers: no exchange between waves, and the softmax state of a row (reference max,
+//    sum) is lane-local (lanes l and l^32 share a row and combine with a permlane32 swap).
+//  * Values O[32 rows x 512 channels] += P Z: 32 v_mfma_f32_32x32x16_bf16, B = Z^T tiles
+//    from two ds_read_b64_tr_b16 transposing reads each; O lives in the 256 AGPRs.
+//  * The reference max of a row is set at its first finite score and never moves, so O is
+//    never rescaled inside the loop (a rare second pass over the segment covers rows whose
+//    maximum later grows by more than 2^64).
+//  * LDS ring of 4 steps (36 KiB each) filled by LDS-DMA (buffer_load_dwordx4 ... lds, 9 per
+//    wave and step, source offsets from a table in LDS), rows XOR-swizzled in 16-B chunks so
+//    that both operand reads are free of bank conflicts. One barrier per step: it publishes
+//    the next step's rows and frees the slot the values of the previous step read.
+//  * Order inside a step: the first value MFMAs of step i (operands read before the
+//    barrier), the score MFMAs of step i+1 (the step's DMA instructions between them), the
+//    remaining value MFMAs of step i with the softmax of step i+1 (VALU) between them.
+//  * The MFMAs are written as inline asm so that O can be pinned to AGPRs while the score
+//    accumulator stays in VGPRs; explicit waits (12+ states) precede every VALU read of an
+//    MFMA result.
+#include "mla_device.h"
+
+namespace mla {
+namespace {
+
+constexpr int kR32Threads = 256;                 // 4 waves, one per SIMD
+constexpr int kR32Slots = 4;                     // LDS ring depth (steps)
+constexpr int kR32Dma = kDmaInstr / 4;           // 9 LDS-DMA instructions per wave and step
+constexpr int kR32LdsBytes = kR32Slots * kBufBytes;   // then 4 x 32 floats of per-row 1/l, 4 votes, DMA offsets
+constexpr int kR32PvLead = 4;                    // value MFMAs of step i before the scores of step i+1
+constexpr int kR32Ring = 4;                      // value operand reads in flight (one MFMA each)
+constexpr int kR32QkRing = 4;                    // score operand reads in flight
+constexpr int kR32OffTab = kR32LdsBytes + 512 + 16;   // DMA offset table: 36 instructions x 64 lanes
+constexpr int kR32LdsTotal = kR32OffTab + kDmaInstr * 64 * 4;
+static_assert(kR32LdsTotal <= 160 * 1024, "LDS budget");
+constexpr float kWindow = 64.f;                  // rows may exceed their reference max by 2^64
+static_assert(kDmaInstr % 4 == 0, "DMA split");
+static_assert(kR32PvLead % kR32Ring == 0 && kR32Ring <= kR32PvLead, "value operand ring turnover");
+static_assert((32 - kR32PvLead) / 2 >= 14, "softmax pieces fit between the value MFMAs");
+
+// 16-B chunk swizzle within 8-chunk groups: physical = logical ^ sw(token). Over 16
+// consecutive tokens of one parity sw is a permutation of 0..7 (conflict-free score reads of
+// 16 tokens x one chunk), and sw(t) ^ sw(t+2) = 4 for t = 0, 1 mod 4 (conflict-free
+// transposing reads of 4 consecutive tokens x 4 chunks).
+__device__ __forceinline__ uint32_t sw32(uint32_t u) { return (((u >> 1) & 1u) << 2) | ((u >> 2) & 3u); }
+
+// Source offset (bytes from the step's first row) of LDS-DMA instruction i = wave + 4n,
+// lane l: it fills LDS chunk position p = 64i + l = 72u + pc, which holds logical chunk
+// pc ^ sw(u) of token u. floor(p / 72) and p mod 72 by full-rate 24-bit multiplies, exact
+// for p < 2304.
+__device__ __forceinline__ uint32_t dma_voff32(int wave, int n, int lane) {
+  const uint32_t p = 64u * (uint32_t)(wave + 4 * n) + (uint32_t)lane;
+  const uint32_t x = __umul24(p, 1821u);
+  const uint32_t u = x >> 17;
+  const uint32_t pc = __umul24(x & 0x1FFFFu, 72u) >> 17;
+  const uint32_t ch = (pc & ~7u) | ((pc & 7u) ^ sw32(u));
+  return __umul24(u, (uint32_t)kRowBytes) + 16u * ch;
+}
+
+// The per-lane source offsets of a wave's 9 DMA instructions are the same for every step;
+// they are computed once into an LDS table (kept in registers they would cost 9 VGPRs,
+// recomputed they cost ~15 VALU per instruction).
+__device__ __forceinline__ void issue32(const i32x4& rsrc, uint32_t lds_slot, int n, uint32_t voff, int wave) {
+  lds_dma_x4(lds_slot + 1024u * (uint32_t)(wave + 4 * n), voff, rsrc);
+}
+
+// v_mfma_f32_32x32x16_bf16 with the accumulator in VGPRs (scores) or AGPRs (values). A VALU
+// write of an operand needs two wait states before an MFMA reads it: the operands here come
+// from LDS/global loads, or (P, the zeroed accumulators) are written by VALU many
+// instructions before their first MFMA.
+__device__ __forceinline__ void mfma_v0(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_a0(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_a(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// An MFMA result may be read by VALU (or v_accvgpr_read) only 12 wait states after the
+// MFMA; 18 here.
+__device__ __forceinline__ void mfma_result_wait(f32x16& s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 1" : "+v"(s));
+}
+// Before the accumulator tiles are read (finalize): 18 wait states after the last MFMA. A
+// plain asm statement plus a scheduling barrier, so that the compiler's AGPR reads stay
+// behind it and are made per use (an asm with the tiles as operands would make it copy all
+// 256 AGPRs to VGPRs at once).
+__device__ __forceinline__ void mfma_results_settle() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 1" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ float max_across_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Per-lane LDS byte addresses of the operand reads of one ring slot (slot offset zoff
+// included), rebuilt from an opaque lane id at each use so that they hold no registers
+// across the step loop.
+// scores: lane reads token l%32, logical chunk 2ks + l/32 -> b[ks % 4] + 128 (ks / 4)
+struct QkAddr { uint32_t b[4]; };
+__device__ __forceinline__ QkAddr qk_addr(uint32_t zoff, int lane) {
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  const uint32_t T = l & 31, h = l >> 5;
+  QkAddr r;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) r.b[x] = zoff + T * kRowBytes + 16 * ((2 * x + h) ^ sw32(T));
+  return r;
+}
+// values: lane (G = l/16, j = l%16) reads token 16q + 8e + 4(G/2) + j/4, channels
+// 32c + 16(G%2) + 4(j%4) .. +3 -> b[e][c % 2] + 16q rows + 128 (c / 2)
+struct PvAddr { uint32_t b[2][2]; };
+__device__ __forceinline__ PvAddr pv_addr(uint32_t zoff, int lane) {
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  const uint32_t G = l >> 4, j = l & 15;
+  PvAddr r;
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int c1 = 0; c1 < 2; ++c1)
+      r.b[e][c1] = zoff + (8 * e + 4 * (G >> 1) + (j >> 2)) * kRowBytes +
+                   16 * ((4 * c1 + 2 * (G & 1) + ((j >> 1) & 1)) ^ (4 * (j >> 3) + 2 * e + (G >> 1))) + 8 * (j & 1);
+  return r;
+}
+
+__global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
+    const __bf16* __restrict__ q_ptr, const char* __restrict__ kv_ptr, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seqlens, const int32_t* __restrict__ plan, float* __restrict__ ws,
+    float* __restrict__ out_ptr, float* __restrict__ lse_ptr, Scalars a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  char __attribute__((address_space(3)))* lds = (char __attribute__((address_space(3)))*)smem_raw;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int worker = xcd_worker();
+  if (plan[kHMagic] != kPlanMagic || plan[kHWorkers] != (int)gridDim.x || plan[kHBatch] != a.batch ||
+      plan[kHSq] != a.s_q || plan[kHHeads] != a.heads || plan[kHCausal] != a.causal)
+    return;
+  const int n_items = plan[kHItems];
+  const int32_t* wr = plan + plan_workers_off(n_items) + kWorkerWords * worker;
+  const int kb = wr[0], pb = wr[1], ke = wr[2], pe = wr[3];
+  int k_last = pe > 0 ? ke : ke - 1;
+  k_last = k_last < n_items - 1 ? k_last : n_items - 1;
+  if (kb >= n_items || k_last < kb) return;
+  const int rows_total = a.s_q * a.heads;
+
+  // Q^T B operand of item k: lane holds query row 32*wave + l%32 of the item's tile, channels
+  // 16ks + 8(l/32) .. +7. Rows past the last query row (a partial tile) load the sequence's
+  // first row: every output column depends on its own row only, and no such row is written.
+  bf16x8 qreg[36];
+  int q_item = -1;
+  auto load_q = [&](int k) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    const int32_t* it = plan + plan_items_off() + kItemWords * k;
+    const int g_row = kRowsPerTile * it[kITile] + 32 * wave + (l & 31);
+    const bool ok = g_row < rows_total;
+    const int jt = ok ? g_row / a.heads : 0;
+    const int hd = ok ? g_row - jt * a.heads : 0;
+    const __bf16* qrow = q_ptr + ((int64_t)(it[kISeq] * a.s_q + jt) * a.heads + hd) * kDqk + 8 * (l >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+    q_item = k;
+  };
+  load_q(kb);
+
+  // ---- load cursor: the first kR32Slots-1 steps are issued up front, then one step per
+  // compute region (its DMA instructions spread between the score MFMAs)
+  LoadCursor lc;
+  cursor_enter(lc, plan, kb, kb, pb, ke, pe);
+  auto settle = [&]() {
+    while (lc.k <= k_last && lc.hh >= lc.hh1) {
+      if (lc.k == k_last) {
+        lc.k = k_last + 1;
+        break;
+      }
+      cursor_enter(lc, plan, lc.k + 1, kb, pb, ke, pe);
+    }
+  };
+  settle();
+  if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
+  int load_slot = 0;
+  auto advance = [&]() {
+    load_slot = load_slot + 1 == kR32Slots ? 0 : load_slot + 1;
+    ++lc.hh;
+    settle();
+    if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
+  };
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
+  // this wave's DMA source offsets: table entry (instruction wave + 4n, lane)
+  const uint32_t __attribute__((address_space(3)))* offtab =
+      (const uint32_t __attribute__((address_space(3)))*)(lds + kR32OffTab) + 64 * wave + lane;
+  {
+    uint32_t __attribute__((address_space(3)))* tab =
+        (uint32_t __attribute__((address_space(3)))*)(lds + kR32OffTab) + 64 * wave + lane;
+#pragma unroll
+    for (int n = 0; n < kR32Dma; ++n) tab[64 * 4 * n] = dma_voff32(wave, n, lane);
+  }
+#pragma unroll 1
+  for (int i = 0; i < kR32Slots - 1; ++i) {   // (zero-record loads past the worker's range)
+    const i32x4 rs = lc.k <= k_last ? cursor_rsrc<false>(lc, a, kv_ptr, nullptr).kv
+                                    : make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
+#pragma unroll
+    for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + load_slot * kBufBytes, n, offtab[64 * 4 * n], wave);
+    advance();
+  }
+
+  int comp_slot = 0;   // ring slot of the segment's current step
+
+#pragma unroll 1
+  for (int k = kb; k <= k_last; ++k) {
+    const Seg sg = seg_of(plan, k, kb, pb, ke, pe);
+    const int32_t* it = plan + plan_items_off() + kItemWords * k;
+
+    // ---- keys visible to this lane's query row 32*wave + l%32
+    int lim = 0;
+    {
+      const int g_row = kRowsPerTile * it[kITile] + 32 * wave + (lane & 31);
+      if (g_row < rows_total) {
+        int t = seqlens[it[kISeq]];
+        t = t < 0 ? 0 : t;
+        const int cap = a.max_pages * kPage;
+        t = t > cap ? cap : t;
+        lim = t;
+        if (a.causal) {
+          lim = t - a.s_q + 1 + g_row / a.heads;
+          lim = lim < 0 ? 0 : (lim > t ? t : lim);
+        }
+      }
+    }
+    if (q_item != k) load_q(k);   // (after an item with no steps)
+
+    f32x16 o[16];
+    float m_run = -INFINITY;   // reference max of the row (log2 domain, integer-valued once set)
+    float m_seen = -INFINITY;  // largest row max seen in the segment
+    float l_run = 0.f;
+    bool window_exceeded = false;
+    const int nsteps = sg.hh1 - sg.hh0;
+
+    // ---- pipeline pieces
+    // score operand t (k-step t)
+    auto qk_read = [&](const QkAddr& ad, int t) -> bf16x8 {
+      return lds_b128(lds + (ad.b[t & 3] + 128 * (t >> 2)));
+    };
+    // value operand t = 16q + c: Z^T[channels 32c ..][16 tokens of k-step q]
+    auto pv_read = [&](const PvAddr& ad, int t) -> bf16x8 {
+      const int q = t >> 4, c = t & 15;
+      const bf16x4 lo = lds_tr16(lds + (ad.b[0][c & 1] + q * 16 * kRowBytes + 128 * (c >> 1)));
+      const bf16x4 hi = lds_tr16(lds + (ad.b[1][c & 1] + q * 16 * kRowBytes + 128 * (c >> 1)));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // Softmax of the scores s of step hh in 8 pieces (so they can sit between MFMAs). The
+    // row's reference max is fixed at its first finite score (rounded up to an integer) and
+    // never moves afterwards, so O is never rescaled: P = 2^(s - ref) stays below 2^64 while
+    // the row max stays within kWindow of the reference (no overflow in fp32 for any
+    // realistic length and magnitude); a row that leaves the window marks the segment for a
+    // second pass with the segment's maximum as the reference. Piece 0 masks and starts the
+    // max, 2 updates the reference, 3..6 exponentiate and round P to bf16, 7 sums.
+    float sm_mx, sm_muse, sm_psum;
+    auto softmax_piece = [&](f32x16& s, int hh, bool live, int piece, bf16x8* pk) {
+      if (piece == 0) {
+        mfma_result_wait(s);
+      } else if (piece <= 4) {
+        const int r0 = 4 * (piece - 1);
+        float mx = piece == 1 ? -INFINITY : sm_mx;
+#pragma unroll
+        for (int r = r0; r < r0 + 4; ++r) mx = fmaxf(mx, s[r]);
+        sm_mx = mx;
+      } else if (piece == 5) {
+        const int key_end = kStep * (hh + 1);
+        if (__ballot(key_end > lim) != 0) {   // a masked step (the sequence's last, or causal rows)
+          const int key0 = kStep * hh + 4 * (lane >> 5);
+          float mx = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[r] = (key0 + 8 * (r >> 2) + (r & 3)) < lim ? s[r] : -INFINITY;
+            mx = fmaxf(mx, s[r]);
+          }
+          sm_mx = mx;
+        }
+        const float mx = max_across_halves(sm_mx) * a.scale_log2;
+        if (live) {
+          m_seen = fmaxf(m_seen, mx);
+          m_run = (m_run == -INFINITY && mx != -INFINITY) ? ceilf(mx) : m_run;
+          window_exceeded = window_exceeded || mx > m_run + kWindow;
+        }
+        sm_muse = (m_run == -INFINITY) ? 0.f : m_run;
+        sm_psum = 0.f;
+      } else if (piece <= 13) {
+        const int r0 = 2 * (piece - 6);
+        float ps = sm_psum;
+#pragma unroll
+        for (int r = r0; r < r0 + 2; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -sm_muse));
+          ps += p;
+          pk[r >> 3][r & 7] = (__bf16)p;
+        }
+        sm_psum = ps;
+      } else {
+        const float psum = sum_across_halves(sm_psum);
+        l_run = live ? l_run + psum : l_run;
+      }
+    };
+    constexpr int kPieces = 15;
+
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) o[c] = f32x16{};
+      if (nsteps > 0) {
+      bf16x8 pcur[2];
+      bf16x8 pring[kR32Ring];   // value operand reads in flight
+      uint32_t zc = (uint32_t)comp_slot * kBufBytes;
+      wait_vmcnt<kR32Dma>();    // data of steps 0 and 1 (step 2 may stay in flight)
+      barrier_lds();
+      // scores and softmax of step 0
+      {
+        f32x16 s;
+        bf16x8 qring[kR32QkRing];
+        const QkAddr qa = qk_addr(zc, lane);
+#pragma unroll
+        for (int t = 0; t < kR32QkRing; ++t) qring[t] = qk_read(qa, t);
+#pragma unroll
+        for (int t = 0; t < 36; ++t) {
+          const bf16x8 cur = qring[t % kR32QkRing];
+          if (t + kR32QkRing < 36) qring[t % kR32QkRing] = qk_read(qa, t + kR32QkRing);
+          if (t == 0) mfma_v0(s, cur, qreg[0]);
+          else mfma_v(s, cur, qreg[t]);
+        }
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) softmax_piece(s, sg.hh0, true, p, pcur);
+        const PvAddr pa = pv_addr(zc, lane);
+#pragma unroll
+        for (int t = 0; t < kR32Ring; ++t) pring[t] = pv_read(pa, t);
+      }
+
+      // Straight-line step body: the scores of step i+1 are computed also after the last
+      // step (on whatever the next slot holds) and discarded, and a region past the end of
+      // the worker's range issues zero-record loads, so that every region has the same
+      // shape and the same DMA count.
+#pragma unroll 1
+      for (int i = 0; i < nsteps; ++i) {
+        const int cs_next = comp_slot + 1 == kR32Slots ? 0 : comp_slot + 1;
+        const uint32_t zn = (uint32_t)cs_next * kBufBytes;
+        const bool live = i + 1 < nsteps;   // step i+1 belongs to this segment
+        const i32x4 rs = lc.k <= k_last ? cursor_rsrc<false>(lc, a, kv_ptr, nullptr).kv
+                                        : make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
+        const uint32_t lslot = lds_u32 + (uint32_t)load_slot * kBufBytes;
+        uint32_t voff = 0;        // source offset of the next DMA instruction (read 3 MFMAs ahead)
+        f32x16 s;                 // scores of step i+1
+        bf16x8 pnext[2];          // P of step i+1
+        // value MFMA t of step i; the operand ring is refilled up to operand `limit`
+        auto pv_mfma = [&](const PvAddr& pa, int t, int limit) {
+          const bf16x8 cur = pring[t % kR32Ring];
+          if (t + kR32Ring < limit) pring[t % kR32Ring] = pv_read(pa, t + kR32Ring);
+          mfma_a(o[t & 15], pcur[t >> 4], cur);
+        };
+        // 1) the first value MFMAs of step i (their first operands were read before the barrier)
+        {
+          const PvAddr pa = pv_addr(zc, lane);
+#pragma unroll
+          for (int t = 0; t < kR32PvLead; ++t) {
+            pv_mfma(pa, t, kR32PvLead);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // 2) scores of step i+1 with the DMA instructions of the step being loaded; the ring
+        //    turns over to the next value operands during the last score MFMAs
+        {
+          bf16x8 qring[kR32QkRing];
+          const QkAddr qa = qk_addr(zn, lane);
+#pragma unroll
+          for (int t = 0; t < kR32QkRing; ++t) qring[t] = qk_read(qa, t);
+          const PvAddr pa = pv_addr(zc, lane);
+#pragma unroll
+          for (int t = 0; t < 36; ++t) {
+            const bf16x8 cur = qring[t % kR32QkRing];
+            if (t + kR32QkRing < 36) qring[t % kR32QkRing] = qk_read(qa, t + kR32QkRing);
+            if (t + kR32Ring >= 36) pring[t % kR32Ring] = pv_read(pa, kR32PvLead + t + kR32Ring - 36);
+            if (t == 0) mfma_v0(s, cur, qreg[0]);
+            else mfma_v(s, cur, qreg[t]);
+            if ((t & 3) == 0) voff = offtab[64 * 4 * (t >> 2)];   // offset of the next DMA instruction
+            if ((t & 3) == 3) issue32(rs, lslot, t >> 2, voff, wave);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // 3) the remaining value MFMAs of step i, the softmax of step i+1 between them
+        {
+          const PvAddr pa = pv_addr(zc, lane);
+#pragma unroll
+          for (int t = kR32PvLead; t < 32; ++t) {
+            pv_mfma(pa, t, 32);
+            // softmax pieces after every other value MFMA, the last one after the last MFMA
+            const int u = t - kR32PvLead;
+            if (u % 2 == 0 && u / 2 < kPieces - 1) softmax_piece(s, sg.hh0 + i + 1, live, u / 2, pnext);
+            if (t == 31) softmax_piece(s, sg.hh0 + i + 1, live, kPieces - 1, pnext);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        pcur[0] = pnext[0];
+        pcur[1] = pnext[1];
+        // the first value operands of step i+1 (its rows were published at the last barrier)
+        {
+          const PvAddr pa = pv_addr(zn, lane);
+#pragma unroll
+          for (int t = 0; t < kR32Ring; ++t) pring[t] = pv_read(pa, t);
+        }
+        // move the load cursor here: its scalar loads share the LDS counter, and the barrier
+        // waits for that counter anyway
+        advance();
+        wait_vmcnt<kR32Dma>();   // everything but this region's DMA: the data of step i+2
+        barrier_lds();
+        comp_slot = cs_next;
+        zc = zn;
+      }
+      }
+      // Did any row of the work-group leave the reference window? (vote through LDS)
+      {
+        int32_t __attribute__((address_space(3)))* vote =
+            (int32_t __attribute__((address_space(3)))*)(lds + kR32LdsBytes + 512);
+        const bool wave_exceeded = __ballot(window_exceeded) != 0;   // (all lanes take part)
+        if (lane == 0) vote[wave] = wave_exceeded ? 1 : 0;
+        barrier_lds();
+        const bool again = (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+        barrier_lds();   // (the votes are read before the area is reused)
+        if (!again || pass == 1) break;
+      }
+      // Second pass over the segment: every row takes the segment's maximum as its reference,
+      // so no P exceeds 1. Wait for the loads in flight (the next item's first steps), then
+      // restart the load cursor at the segment's first step in an empty ring.
+      wait_vmcnt<0>();
+      barrier_lds();
+      m_run = (m_seen == -INFINITY) ? -INFINITY : ceilf(m_seen);
+      l_run = 0.f;
+      window_exceeded = false;
+      cursor_enter(lc, plan, k, kb, pb, ke, pe);
+      settle();
+      if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
+      load_slot = 0;
+      comp_slot = 0;
+#pragma unroll 1
+      for (int j = 0; j < kR32Slots - 1; ++j) {
+        const i32x4 rs = lc.k <= k_last ? cursor_rsrc<false>(lc, a, kv_ptr, nullptr).kv
+                                        : make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
+#pragma unroll
+        for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + load_slot * kBufBytes, n, offtab[64 * 4 * n], wave);
+        advance();
+      }
+    }
+
+    // ---- finalize (wave-local): out = O / l and lse = m + log2(l), or a normalised bf16
+    // partial in register order plus lse for items the plan split. O tile c holds, in lane l
+    // and register r, row 8(r/4) + 4(l/32) + r%4 of the wave's 32 rows and channel
+    // 32c + l%32; the per-row 1/l comes from the row's lane through LDS.
+    {
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      const int32_t* itf = plan + plan_items_off() + kItemWords * k;
+      const int f_seq = itf[kISeq], f_tile = itf[kITile];
+      const bool split = itf[kINsplits] > 1;
+      const int slot = split ? itf[kISlot] + (worker - itf[kIOwner]) : 0;
+      const int row0 = kRowsPerTile * f_tile + 32 * wave;   // the wave's first row in the item
+      float __attribute__((address_space(3)))* inv_s =
+          (float __attribute__((address_space(3)))*)(lds + kR32LdsBytes) + 32 * wave;
+      if (l < 32) inv_s[l] = l_run > 0.f ? 1.f / l_run : 0.f;
+      f32x4 inv4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) inv4[j] = *(const f32x4 __attribute__((address_space(3)))*)(inv_s + 8 * j + 4 * (l >> 5));
+      mfma_results_settle();
+      if (split) {
+        char* part = reinterpret_cast<char*>(ws) + (int64_t)slot * kSlotBytes;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          bf16x8 v0, v1;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            v0[r] = (__bf16)(o[c][r] * inv4[r >> 2][r & 3]);
+            v1[r] = (__bf16)(o[c][8 + r] * inv4[2 + (r >> 2)][r & 3]);
+          }
+          char* dst = part + 32 * (int64_t)((wave * 16 + c) * 64 + l);
+          *reinterpret_cast<bf16x8*>(dst) = v0;
+          *reinterpret_cast<bf16x8*>(dst + 16) = v1;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int grow = row0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+          const bool ok = grow < rows_total;
+          const int jt = ok ? grow / a.heads : 0, hd = ok ? grow - jt * a.heads : 0;
+          float* dst = out_ptr + ((int64_t)(f_seq * a.s_q + jt) * a.heads + hd) * kLat + (l & 31);
+          const float sc = inv4[r >> 2][r & 3];
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const float v = o[c][r] * sc;
+            if (ok) dst[32 * c] = v;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      const int grow = row0 + (l & 31);
+      const int row = 32 * wave + (l & 31);
+      if (l < 32 && grow < rows_total) {
+        const float m = (m_run == -INFINITY) ? 0.f : m_run;
+        const float lse_v = l_run > 0.f ? (m + __log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+        if (split) {
+          reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (int64_t)slot * kSlotBytes + kSlotPartBytes)[row] = lse_v;
+        } else {
+          const int jt = grow / a.heads, hd = grow - jt * a.heads;
+          lse_ptr[(int64_t)(f_seq * a.s_q + jt) * a.heads + hd] = lse_v;
+        }
+      } else if (l < 32 && split) {
+        reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (int64_t)slot * kSlotBytes + kSlotPartBytes)[row] = -INFINITY;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the next item's query rows: the youngest loads in flight, so waiting for them (at
+    // their first use) leaves no ring step behind
+    __builtin_amdgcn_sched_barrier(0);
+    if (k < k_last) load_q(k + 1);
+  }
+}
+
+// Merge the partials of split items written by decode_rows32_kernel: lse = log sum_k e^{lse_k},
+// out = sum_k e^{lse_k - lse} O_k (max-shifted; parts with lse = -inf carry no weight).
+// One block per (split item, 32-row group w, 128-channel quarter cq). Fragment (w, c, lane)
+// of a part is 32 contiguous bytes: 16 bf16, value r at row 32w + 8(r/4) + 4(lane/32) + r%4
+// and channel 32c + lane%32, so a block reads 8 contiguous KiB per part. The data loads of
+// the first parts are issued before the weights are formed; the merged rows leave through
+// LDS as 512-B row segments.
+constexpr int kCmbThreads = 256;
+constexpr int kCmbMaxSplits = 256;   // parts merged per pass over the weights
+constexpr int kCmbBatch = 4;         // parts whose data is in flight together
+
+__global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32_t* __restrict__ plan,
+                                                                     const char* __restrict__ ws,
+                                                                     float* __restrict__ out,
+                                                                     float* __restrict__ lse, int s_q, int heads) {
+  __shared__ __attribute__((aligned(16))) float wts[kCmbMaxSplits][32];   // [part][row]
+  __shared__ float tile_out[32][128 + 4];
+  __shared__ __attribute__((aligned(16))) float row_resc[32];
+  __shared__ __attribute__((aligned(16))) float row_t[32];
+  __shared__ float row_m[32];
+  if (plan[kHMagic] != kPlanMagic) return;
+  const int n_split = plan[kHSplitItems];
+  const int n_items = plan[kHItems];
+  if ((int)blockIdx.x >= n_split) return;
+  const int k = plan[plan_split_off(n_items, plan[kHWorkers]) + blockIdx.x];
+  const int32_t* it = plan + plan_items_off() + kItemWords * k;
+  const int seq = it[kISeq], tile = it[kITile], ns_all = it[kINsplits], slot0 = it[kISlot];
+  const int rows_total = s_q * heads;
+  const int w = blockIdx.y, cq = blockIdx.z;
+  if (kRowsPerTile * tile + 32 * w >= rows_total) return;
+  const int tid = threadIdx.x;
+  const int c = 4 * cq + (tid >> 6), ln = tid & 63, h = ln >> 5;
+  const int64_t frag = 32 * (int64_t)((w * 16 + c) * 64 + ln);
+  // this thread's rows: 8j + 4h + v for register r = 4j + v
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  float m_old = -INFINITY, t_old = 0.f;   // per row, kept by threads tid < 32
+  for (int s0 = 0; s0 < ns_all; s0 += kCmbMaxSplits) {
+    const int ns = ns_all - s0 < kCmbMaxSplits ? ns_all - s0 : kCmbMaxSplits;
+    // data of the first parts in flight while the weights are formed
+    bf16x8 v[kCmbBatch][2];
+#pragma unroll
+    for (int b = 0; b < kCmbBatch; ++b)
+      if (b < ns) {
+        const char* p = ws + (int64_t)(slot0 + s0 + b) * kSlotBytes + frag;
+        v[b][0] = *reinterpret_cast<const bf16x8*>(p);
+        v[b][1] = *reinterpret_cast<const bf16x8*>(p + 16);
+      }
+    __syncthreads();
+    for (int idx = tid; idx < 32 * ns; idx += kCmbThreads) {
+      const int rr = idx & 31, sp = idx >> 5;
+      wts[sp][rr] = reinterpret_cast<const float*>(ws + (int64_t)(slot0 + s0 + sp) * kSlotBytes +
+                                                   kSlotPartBytes)[32 * w + rr];
+    }
+    __syncthreads();
+    if (tid < 32) {
+      float m = m_old;
+      for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, wts[sp][tid]);
+      const float safe = m == -INFINITY ? 0.f : m;
+      const float resc = m_old == -INFINITY ? 0.f : __expf(m_old - safe);
+      float tot = t_old * resc;
+      for (int sp = 0; sp < ns; ++sp) {
+        const float lv = wts[sp][tid];
+        const float wgt = lv == -INFINITY ? 0.f : __expf(lv - safe);
+        wts[sp][tid] = wgt;
+        tot += wgt;
+      }
+      m_old = m;
+      t_old = tot;
+      row_resc[tid] = resc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 rs4 = *reinterpret_cast<const f32x4*>(&row_resc[8 * j + 4 * h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * j + e] *= rs4[e];
+    }
+    for (int b0 = 0; b0 < ns; b0 += kCmbBatch) {
+      if (b0 > 0) {
+#pragma unroll
+        for (int b = 0; b < kCmbBatch; ++b)
+          if (b0 + b < ns) {
+            const char* p = ws + (int64_t)(slot0 + s0 + b0 + b) * kSlotBytes + frag;
+            v[b][0] = *reinterpret_cast<const bf16x8*>(p);
+            v[b][1] = *reinterpret_cast<const bf16x8*>(p + 16);
+          }
+      }
+#pragma unroll
+      for (int b = 0; b < kCmbBatch; ++b)
+        if (b0 + b < ns) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&wts[b0 + b][8 * j + 4 * h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * j + e;
+              acc[r] += w4[e] * (float)v[b][r >> 3][r & 7];
+            }
+          }
+        }
+    }
+  }
+  if (tid < 32) {
+    row_t[tid] = t_old;
+    row_m[tid] = m_old;
+  }
+  __syncthreads();
+  {
+    const int cl = 32 * (c - 4 * cq) + (ln & 31);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 t4 = *reinterpret_cast<const f32x4*>(&row_t[8 * j + 4 * h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = t4[e];
+        tile_out[8 * j + 4 * h + e][cl] = acc[4 * j + e] * (t > 0.f ? 1.f / t : 0.f);
+      }
+    }
+  }
+  __syncthreads();
+  // 32 rows x 128 channels: 32 float4 per row
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int idx = tid + kCmbThreads * j;
+    const int rr = idx >> 5, c4 = (idx & 31) * 4;
+    const int grow = kRowsPerTile * tile + 32 * w + rr;
+    if (grow >= rows_total) continue;
+    const int jt = grow / heads, hd = grow - jt * heads;
+    const int64_t orow = (int64_t)(seq * s_q + jt) * heads + hd;
+    *reinterpret_cast<f32x4*>(out + orow * kLat + 128 * cq + c4) = *reinterpret_cast<const f32x4*>(&tile_out[rr][c4]);
+    if (cq == 0 && c4 == 0) {
+      const float t = row_t[rr];
+      lse[orow] = t > 0.f ? row_m[rr] + __logf(t) : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_rows32(const DecodeArgs& a, hipStream_t stream) {
+  static thread_local int configured = -1;   // the LDS opt-in is per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (configured != dev) {
+    e = hipFuncSetAttribute((const void*)decode_rows32_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kR32LdsTotal);
+    if (e != hipSuccess) return e;
+    configured = dev;
+  }
+  hipLaunchKernelGGL(decode_rows32_kernel, dim3(a.workers), dim3(kR32Threads), kR32LdsTotal, stream,
+                     reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const char*>(a.kv), a.block_table,
+                     a.seqlens, a.plan, a.ws, a.out, a.lse, scalars_of(a));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream) {
+  const int max_split = a.workers;   // split items <= active workers - 1
+  hipLaunchKernelGGL(combine_rows32_kernel, dim3(max_split, kRowsPerTile / 32, 4), dim3(kCmbThreads), 0, stream,
+                     a.plan, reinterpret_cast<const char*>(a.ws), a.out, a.lse, a.s_q, a.heads);
+  return hipGetLastError();
+}
+
+}  // namespace mla

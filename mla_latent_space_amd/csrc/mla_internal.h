@@ -70,8 +70,9 @@ struct DecodeArgs {
   float* lse;
 };
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_rows32(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace mla

@@ -137,6 +137,37 @@ def test_empty_visible_sets():
     assert (out[0] == 0).all()
 
 
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("W", [1, 5, 256])
+def test_scores_growing_past_the_reference_window(W):
+    """Scores that grow along the sequence by hundreds of log2 units: a row's maximum leaves
+    the window above its first-step reference, so the kernel must take its second pass over
+    the segment with the segment's maximum as the reference (else P overflows)."""
+    w = wl.make_workload("ramp", batch=2, s_q=1, heads=32, seqlens=[600, 3000], seed=31, poison=False)
+    q = _bits_to_f32(w.q)
+    q[:, :, :16, :64] = 64.0            # heads 0..15 align with the ramp direction
+    w.q = _bf16_bits(q)
+    kv = _bits_to_f32(w.kv)
+    for b, t in enumerate(w.seqlens):
+        for j in range(t):
+            page, slot = w.block_table[b, j // 64], j % 64
+            kv[page, slot, :64] += 1.0 * j / max(1, t - 1)   # score ramp of 4096 (~426 log2 units)
+    w.kv = _bf16_bits(kv)
+    _say("ramp W", W)
+    ro, rl = _oracle_all(w)
+    d = Dev(w)
+    out, lse = d.run(W)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, BF16_TOL, f"ramp W={W}")
+
+
 def test_plan_independence_and_bitwise_repeat():
     w = wl.make_workload("indep", batch=5, s_q=1, heads=128, seqlens=[5000, 64, 700, 1, 2049], seed=25)
     d = Dev(w)
