@@ -49,7 +49,7 @@ static_assert(kR32LdsTotal <= 160 * 1024, "LDS budget");
 constexpr float kWindow = 64.f;                  // rows may exceed their reference max by 2^64
 static_assert(kDmaInstr % 4 == 0, "DMA split");
 static_assert(kR32PvLead % kR32Ring == 0 && kR32Ring <= kR32PvLead, "value operand ring turnover");
-static_assert((32 - kR32PvLead) / 2 >= 14, "softmax pieces fit between the value MFMAs");
+static_assert(32 - kR32PvLead >= 23, "softmax pieces fit between the value MFMAs");
 
 // 16-B chunk swizzle within 8-chunk groups: physical = logical ^ sw(token). Over 16
 // consecutive tokens of one parity sw is a permutation of 0..7 (conflict-free score reads of
@@ -187,8 +187,6 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     for (int ks = 0; ks < 36; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
     q_item = k;
   };
-  load_q(kb);
-
   // ---- load cursor: the first kR32Slots-1 steps are issued up front, then one step per
   // compute region (its DMA instructions spread between the score MFMAs)
   LoadCursor lc;
@@ -221,6 +219,8 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
 #pragma unroll
     for (int n = 0; n < kR32Dma; ++n) tab[64 * 4 * n] = dma_voff32(wave, n, lane);
   }
+  // the first step, then the first item's query rows, then two more steps: the first scores
+  // wait only for the first step and the queries
 #pragma unroll 1
   for (int i = 0; i < kR32Slots - 1; ++i) {   // (zero-record loads past the worker's range)
     const i32x4 rs = lc.k <= k_last ? cursor_rsrc<false>(lc, a, kv_ptr, nullptr).kv
@@ -228,6 +228,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
 #pragma unroll
     for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + load_slot * kBufBytes, n, offtab[64 * 4 * n], wave);
     advance();
+    if (i == 0) load_q(kb);
   }
 
   int comp_slot = 0;   // ring slot of the segment's current step
@@ -274,13 +275,15 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       const bf16x4 hi = lds_tr16(lds + (ad.b[1][c & 1] + q * 16 * kRowBytes + 128 * (c >> 1)));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    // Softmax of the scores s of step hh in 8 pieces (so they can sit between MFMAs). The
-    // row's reference max is fixed at its first finite score (rounded up to an integer) and
-    // never moves afterwards, so O is never rescaled: P = 2^(s - ref) stays below 2^64 while
-    // the row max stays within kWindow of the reference (no overflow in fp32 for any
-    // realistic length and magnitude); a row that leaves the window marks the segment for a
-    // second pass with the segment's maximum as the reference. Piece 0 masks and starts the
-    // max, 2 updates the reference, 3..6 exponentiate and round P to bf16, 7 sums.
+    // Softmax of the scores s of step hh in small pieces, each about one MFMA's worth of
+    // VALU, so that they can sit between the value MFMAs. The row's reference max is fixed
+    // at its first finite score (rounded up to an integer) and never moves afterwards, so O
+    // is never rescaled: P = 2^(s - ref) stays below 2^64 while the row max stays within
+    // kWindow of the reference (no overflow in fp32 for any realistic length and magnitude);
+    // a row that leaves the window marks the segment for a second pass with the segment's
+    // maximum as the reference. Pieces: 0 waits for the scores, 1..4 take the max, 5 masks
+    // (a masked step only) and updates the reference, 6..21 exponentiate one value each and
+    // round P to bf16, 22 sums.
     float sm_mx, sm_muse, sm_psum;
     auto softmax_piece = [&](f32x16& s, int hh, bool live, int piece, bf16x8* pk) {
       if (piece == 0) {
@@ -311,22 +314,17 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         }
         sm_muse = (m_run == -INFINITY) ? 0.f : m_run;
         sm_psum = 0.f;
-      } else if (piece <= 13) {
-        const int r0 = 2 * (piece - 6);
-        float ps = sm_psum;
-#pragma unroll
-        for (int r = r0; r < r0 + 2; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -sm_muse));
-          ps += p;
-          pk[r >> 3][r & 7] = (__bf16)p;
-        }
-        sm_psum = ps;
+      } else if (piece <= 21) {
+        const int r = piece - 6;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -sm_muse));
+        sm_psum += p;
+        pk[r >> 3][r & 7] = (__bf16)p;
       } else {
         const float psum = sum_across_halves(sm_psum);
         l_run = live ? l_run + psum : l_run;
       }
     };
-    constexpr int kPieces = 15;
+    constexpr int kPieces = 23;
 
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
@@ -336,7 +334,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       bf16x8 pcur[2];
       bf16x8 pring[kR32Ring];   // value operand reads in flight
       uint32_t zc = (uint32_t)comp_slot * kBufBytes;
-      wait_vmcnt<kR32Dma>();    // data of steps 0 and 1 (step 2 may stay in flight)
+      wait_vmcnt<2 * kR32Dma>();   // data of step 0 (steps 1 and 2 may stay in flight)
       barrier_lds();
       // scores and softmax of step 0
       {
@@ -358,6 +356,8 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
 #pragma unroll
         for (int t = 0; t < kR32Ring; ++t) pring[t] = pv_read(pa, t);
       }
+      wait_vmcnt<kR32Dma>();      // data of step 1, for the first region's scores
+      barrier_lds();
 
       // Straight-line step body: the scores of step i+1 are computed also after the last
       // step (on whatever the next slot holds) and discarded, and a region past the end of
@@ -415,10 +415,9 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
 #pragma unroll
           for (int t = kR32PvLead; t < 32; ++t) {
             pv_mfma(pa, t, 32);
-            // softmax pieces after every other value MFMA, the last one after the last MFMA
+            // one softmax piece after each value MFMA
             const int u = t - kR32PvLead;
-            if (u % 2 == 0 && u / 2 < kPieces - 1) softmax_piece(s, sg.hh0 + i + 1, live, u / 2, pnext);
-            if (t == 31) softmax_piece(s, sg.hh0 + i + 1, live, kPieces - 1, pnext);
+            if (u < kPieces) softmax_piece(s, sg.hh0 + i + 1, live, u, pnext);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -473,8 +472,8 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       }
     }
 
-    // ---- finalize (wave-local): out = O / l and lse = m + log2(l), or a normalised bf16
-    // partial in register order plus lse for items the plan split. O tile c holds, in lane l
+    // ---- finalize (wave-local): out = O / l and lse = m + log2(l), or, for items the plan
+    // split, the unnormalised bf16 partial in register order plus (m, l). O tile c holds, in lane l
     // and register r, row 8(r/4) + 4(l/32) + r%4 of the wave's 32 rows and channel
     // 32c + l%32; the per-row 1/l comes from the row's lane through LDS.
     {
@@ -498,9 +497,9 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         for (int c = 0; c < 16; ++c) {
           bf16x8 v0, v1;
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            v0[r] = (__bf16)(o[c][r] * inv4[r >> 2][r & 3]);
-            v1[r] = (__bf16)(o[c][8 + r] * inv4[2 + (r >> 2)][r & 3]);
+          for (int r = 0; r < 8; ++r) {   // unnormalised: the combine divides by the denominator
+            v0[r] = (__bf16)o[c][r];
+            v1[r] = (__bf16)o[c][8 + r];
           }
           char* dst = part + 32 * (int64_t)((wave * 16 + c) * 64 + l);
           *reinterpret_cast<bf16x8*>(dst) = v0;
@@ -525,17 +524,20 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       }
       const int grow = row0 + (l & 31);
       const int row = 32 * wave + (l & 31);
-      if (l < 32 && grow < rows_total) {
+      if (split) {
+        // the partial's reference max (log2 units; -inf for a row with no visible key) and
+        // softmax denominator
+        if (l < 32) {
+          float* stat = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (int64_t)slot * kSlotBytes + kSlotPartBytes);
+          const bool any = grow < rows_total && l_run > 0.f;
+          stat[row] = any ? m_run : -INFINITY;
+          stat[kRowsPerTile + row] = any ? l_run : 0.f;
+        }
+      } else if (l < 32 && grow < rows_total) {
         const float m = (m_run == -INFINITY) ? 0.f : m_run;
         const float lse_v = l_run > 0.f ? (m + __log2f(l_run)) * 0.6931471805599453f : -INFINITY;
-        if (split) {
-          reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (int64_t)slot * kSlotBytes + kSlotPartBytes)[row] = lse_v;
-        } else {
-          const int jt = grow / a.heads, hd = grow - jt * a.heads;
-          lse_ptr[(int64_t)(f_seq * a.s_q + jt) * a.heads + hd] = lse_v;
-        }
-      } else if (l < 32 && split) {
-        reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (int64_t)slot * kSlotBytes + kSlotPartBytes)[row] = -INFINITY;
+        const int jt = grow / a.heads, hd = grow - jt * a.heads;
+        lse_ptr[(int64_t)(f_seq * a.s_q + jt) * a.heads + hd] = lse_v;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -546,22 +548,25 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   }
 }
 
-// Merge the partials of split items written by decode_rows32_kernel: lse = log sum_k e^{lse_k},
-// out = sum_k e^{lse_k - lse} O_k (max-shifted; parts with lse = -inf carry no weight).
+// Merge the partials of split items written by decode_rows32_kernel. Part k of a row holds
+// O_k (unnormalised, relative to its reference max m_k, log2 units) and its denominator l_k:
+// with M = max_k m_k and a_k = 2^(m_k - M), out = sum_k a_k O_k / sum_k a_k l_k and
+// lse = (M + log2 sum_k a_k l_k) ln 2 (parts with no visible key have m_k = -inf, weight 0).
 // One block per (split item, 32-row group w, 128-channel quarter cq). Fragment (w, c, lane)
 // of a part is 32 contiguous bytes: 16 bf16, value r at row 32w + 8(r/4) + 4(lane/32) + r%4
 // and channel 32c + lane%32, so a block reads 8 contiguous KiB per part. The data loads of
 // the first parts are issued before the weights are formed; the merged rows leave through
 // LDS as 512-B row segments.
 constexpr int kCmbThreads = 256;
-constexpr int kCmbMaxSplits = 256;   // parts merged per pass over the weights
+constexpr int kCmbMaxSplits = 64;    // parts merged per pass over the weights (LDS: 2 x 8 KiB)
 constexpr int kCmbBatch = 4;         // parts whose data is in flight together
 
 __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32_t* __restrict__ plan,
                                                                      const char* __restrict__ ws,
                                                                      float* __restrict__ out,
                                                                      float* __restrict__ lse, int s_q, int heads) {
-  __shared__ __attribute__((aligned(16))) float wts[kCmbMaxSplits][32];   // [part][row]
+  __shared__ __attribute__((aligned(16))) float wts[kCmbMaxSplits][32];   // [part][row]: m_k, then weights
+  __shared__ float dens[kCmbMaxSplits][32];                               // [part][row]: l_k
   __shared__ float tile_out[32][128 + 4];
   __shared__ __attribute__((aligned(16))) float row_resc[32];
   __shared__ __attribute__((aligned(16))) float row_t[32];
@@ -598,21 +603,22 @@ __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32
     __syncthreads();
     for (int idx = tid; idx < 32 * ns; idx += kCmbThreads) {
       const int rr = idx & 31, sp = idx >> 5;
-      wts[sp][rr] = reinterpret_cast<const float*>(ws + (int64_t)(slot0 + s0 + sp) * kSlotBytes +
-                                                   kSlotPartBytes)[32 * w + rr];
+      const float* stat = reinterpret_cast<const float*>(ws + (int64_t)(slot0 + s0 + sp) * kSlotBytes + kSlotPartBytes);
+      wts[sp][rr] = stat[32 * w + rr];
+      dens[sp][rr] = stat[kRowsPerTile + 32 * w + rr];
     }
     __syncthreads();
     if (tid < 32) {
       float m = m_old;
       for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, wts[sp][tid]);
       const float safe = m == -INFINITY ? 0.f : m;
-      const float resc = m_old == -INFINITY ? 0.f : __expf(m_old - safe);
+      const float resc = m_old == -INFINITY ? 0.f : exp2f(m_old - safe);
       float tot = t_old * resc;
       for (int sp = 0; sp < ns; ++sp) {
-        const float lv = wts[sp][tid];
-        const float wgt = lv == -INFINITY ? 0.f : __expf(lv - safe);
+        const float mk = wts[sp][tid];
+        const float wgt = mk == -INFINITY ? 0.f : exp2f(mk - safe);
         wts[sp][tid] = wgt;
-        tot += wgt;
+        tot += wgt * dens[sp][tid];
       }
       m_old = m;
       t_old = tot;
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32
     *reinterpret_cast<f32x4*>(out + orow * kLat + 128 * cq + c4) = *reinterpret_cast<const f32x4*>(&tile_out[rr][c4]);
     if (cq == 0 && c4 == 0) {
       const float t = row_t[rr];
-      lse[orow] = t > 0.f ? row_m[rr] + __logf(t) : -INFINITY;
+      lse[orow] = t > 0.f ? (row_m[rr] + __log2f(t)) * 0.6931471805599453f : -INFINITY;
     }
   }
 }

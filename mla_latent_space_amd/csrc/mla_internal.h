@@ -44,11 +44,12 @@ __host__ __device__ inline int tiles_per_seq(int s_q, int heads) {
   return (s_q * heads + kRowsPerTile - 1) / kRowsPerTile;
 }
 
-// Workspace: per partial slot (one split part of a 128-row item), the normalised partial
-// out as bf16 in the value MFMAs' register order (128 x 512 values, see the decode kernel's
-// finalize), then 128 fp32 lse.
+// Workspace: per partial slot (one split part of a 128-row item), the partial out as bf16 in
+// the value MFMAs' register order (128 x 512 values, see the decode kernels' finalize), then
+// two fp32 per row: bf16 cache kernel: the unnormalised partial's reference max (log2 units)
+// and its softmax denominator; fp8 cache kernel: a normalised partial's lse (first half).
 constexpr int64_t kSlotPartBytes = (int64_t)kRowsPerTile * kLat * 2;
-constexpr int64_t kSlotBytes = kSlotPartBytes + (int64_t)kRowsPerTile * 4;
+constexpr int64_t kSlotBytes = kSlotPartBytes + (int64_t)kRowsPerTile * 8;
 
 hipError_t launch_plan(const int32_t* seqlens, int batch, int s_q, int heads, int causal, int workers,
                        int32_t* plan, hipStream_t stream);

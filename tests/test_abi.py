@@ -42,7 +42,7 @@ def test_sizes():
     assert mla.plan_bytes(64, 1, 128, W) == 4 * (16 + 8 * n + 4 * W + n)
     assert mla.plan_bytes(32, 16, 128, W) == 4 * (16 + 9 * 32 * 16 + 4 * W)
     # per split part: 128 x 512 bf16 partial out + 128 fp32 lse
-    assert mla.workspace_bytes(64, 1, 128, W) == 2 * (W - 1) * (128 * 512 * 2 + 128 * 4)
+    assert mla.workspace_bytes(64, 1, 128, W) == 2 * (W - 1) * (128 * 512 * 2 + 128 * 8)
     assert mla.workspace_bytes(64, 1, 128, 1) == 0
     for bad in [(0, 1, 128, W), (4, 0, 128, W), (4, 1, 96, W), (4, 65, 128, W), (4, 1, 128, 0), (4, 1, 128, 5000),
                 (20000, 1, 128, W), (2000, 16, 128, W)]:
