@@ -55,6 +55,10 @@ def describe(w) -> str:
             f"in shuffled order{', causal' if w.causal else ''}, fp32 out+lse")
 
 
+# kernel sources whose sha256 keys the committed HBM-traffic record
+TRAFFIC_SOURCES = ("mla_device.h", "mla_decode.hip", "mla_decode_rows32.hip", "mla_plan.hip")
+
+
 def traffic_from_profile(kernel_srcs, key):
     """HBM traffic of the decode call from a committed rocprofv3 PMC summary, only if it was
     taken on the current kernel sources (sha256 of the .hip files)."""
@@ -193,7 +197,7 @@ def main():
     ai = flops / byts
     bound_us = max(byts / (PEAK_HBM_GBPS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
     bound = "hbm" if byts / (PEAK_HBM_GBPS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12) else "mfma"
-    srcs = [os.path.join(ROOT, "mla_latent_space_amd", "csrc", f) for f in ("mla_decode.hip", "mla_plan.hip")]
+    srcs = [os.path.join(ROOT, "mla_latent_space_amd", "csrc", f) for f in TRAFFIC_SOURCES]
     traffic = traffic_from_profile(srcs, args.workload)
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
