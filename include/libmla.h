@@ -94,8 +94,10 @@ size_t mla_workspace_bytes(int32_t batch, int32_t s_q, int32_t heads, int32_t nu
  *
  * Work items are (sequence, 128-row tile of the s_q*heads query rows). Items are sorted
  * by page count, longest first (stable), laid end to end with a fixed per-item overhead
- * in page units, and cut into num_workers contiguous runs of equal cost; an item cut
- * across runs is "split" and its runs are merged by log-sum-exp in mla_decode_fwd.
+ * in page units spread evenly over the item's pages, and cut into at most num_workers
+ * contiguous runs of equal cost (fewer for very small batches, so that no run inside a
+ * split item is empty); an item cut across runs is "split" and its runs are merged by
+ * log-sum-exp in mla_decode_fwd.
  * Runs entirely on the device (one work-group); no host synchronisation.
  *
  * seqlens   device int32 [batch]: cached tokens per sequence (incl. the s_q new ones).

@@ -7,7 +7,9 @@
 // (up to 1024 items by a rank sort, beyond that by a two-pass LSD radix sort in LDS with
 // 8-bit digits and wave ballots for the stable rank),
 // costed as overhead + pages, prefix-summed, and cut into equal-cost contiguous runs,
-// one per worker (one persistent decode work-group per compute unit).
+// one per worker (one persistent decode work-group per compute unit). An item's overhead
+// is spread evenly over its pages (page j of item k starts at C_k + j (overhead + pages) /
+// pages), so equal items cut into equal page counts.
 #include "mla_internal.h"
 
 namespace mla {
@@ -61,8 +63,10 @@ __device__ inline int block_exclusive_scan(int x, int* scratch, int* total) {
   return wave_off + incl - x;
 }
 
-__device__ inline int worker_of(int64_t x, int64_t total, int64_t W) {
-  return (int)(((x + 1) * W - 1) / total);
+// Worker of page j of an item with cost prefix ck and `pages` pages: floor(x W / C) for the
+// page's start x = ck + j (overhead + pages) / pages, in integers.
+__device__ inline int page_worker(int64_t ck, int64_t pages, int64_t j, int64_t total, int64_t W) {
+  return (int)(((ck * pages + j * (kPlanOverhead + pages)) * W) / (total * pages));
 }
 
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restrict__ seqlens, int batch, int s_q,
@@ -185,14 +189,17 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
   }
   __syncthreads();
   const int64_t C = total;
-  const int64_t Weff = (int64_t)W < C ? (int64_t)W : C;
+  // fewer workers than cost units / (1 + overhead / 2): every worker interval is at least
+  // as long as one page of an item of two or more pages
+  const int64_t Wcap = (2 * C) / (2 + kPlanOverhead);
+  const int64_t Weff = (int64_t)W < Wcap ? (int64_t)W : Wcap;
 
   // owners, splits; slots and split-list positions by one packed scan
   int local_pack = 0;
   for (int k = lo; k < hi; ++k) {
     const int pages = 0xFFFF - (int)(src[k] >> 16);
-    const int first = worker_of((int64_t)cost[k] + kPlanOverhead, C, Weff);
-    const int last = worker_of((int64_t)cost[k] + kPlanOverhead + pages - 1, C, Weff);
+    const int first = page_worker(cost[k], pages, 0, C, Weff);
+    const int last = page_worker(cost[k], pages, pages - 1, C, Weff);
     const int ns = last - first + 1;
     local_pack += ns > 1 ? ((ns << 16) | 1) : 0;
   }
@@ -205,8 +212,8 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     const int idx = (int)(key & 0xFFFF);
     int sq, tl, vis, pages;
     item_shape(seqlens, idx, tiles, s_q, heads, causal, &sq, &tl, &vis, &pages);
-    const int first = worker_of((int64_t)cost[k] + kPlanOverhead, C, Weff);
-    const int last = worker_of((int64_t)cost[k] + kPlanOverhead + pages - 1, C, Weff);
+    const int first = page_worker(cost[k], pages, 0, C, Weff);
+    const int last = page_worker(cost[k], pages, pages - 1, C, Weff);
     const int ns = last - first + 1;
     int32_t* it = items + kItemWords * k;
     it[kISeq] = sq;
@@ -220,22 +227,25 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     if (ns > 1) split_list[pack_run & 0xFFFF] = k;
     pack_run += ns > 1 ? ((ns << 16) | 1) : 0;
   }
-  // workers: start(w) = (item holding position floor(w C / Weff), page offset)
+  // workers: start(w) = the first page whose start position is >= w C / Weff
   int32_t* workers = plan + plan_workers_off(n);
   for (int w = tid; w < W; w += nthreads) {
     int sk[2], sp[2];
     for (int e = 0; e < 2; ++e) {
       const int64_t ww = w + e;
       if (ww >= Weff) { sk[e] = n; sp[e] = 0; continue; }
-      const int64_t b = (ww * C) / Weff;
-      int l = 0, r = n - 1;   // largest k with cost[k] <= b
+      const int64_t b = ww * C;   // position w C / Weff, times Weff
+      int l = 0, r = n - 1;       // largest k with cost[k] Weff <= b
       while (l < r) {
         const int m = (l + r + 1) >> 1;
-        if ((int64_t)cost[m] <= b) l = m; else r = m - 1;
+        if ((int64_t)cost[m] * Weff <= b) l = m; else r = m - 1;
       }
-      sk[e] = l;
-      const int64_t off = b - cost[l] - kPlanOverhead;
-      sp[e] = off > 0 ? (int)off : 0;
+      const int64_t pages = 0xFFFF - (int64_t)(src[l] >> 16);
+      const int64_t num = (b - (int64_t)cost[l] * Weff) * pages;
+      const int64_t den = Weff * (kPlanOverhead + pages);
+      const int64_t j = (num + den - 1) / den;   // smallest j whose start is >= w C / Weff
+      sk[e] = j < pages ? l : l + 1;
+      sp[e] = j < pages ? (int)j : 0;
     }
     int32_t* wr = workers + kWorkerWords * w;
     wr[0] = sk[0]; wr[1] = sp[0]; wr[2] = sk[1]; wr[3] = sp[1];

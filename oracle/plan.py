@@ -15,14 +15,19 @@ the device planner can be checked against it bit for bit:
    some worker writes its zero output.
 2. Order. Items sorted by page count, longest first; ties keep item order
    (sequence-major, tile-minor). (A stable sort; the device uses an LSD radix sort.)
-3. Cost. Item k costs ``overhead + pages_k`` units, where ``overhead`` stands for
+3. Cost. Item k costs ``c_k = overhead + pages_k`` units, where ``overhead`` stands for
    loading the item's queries and writing its output. C_k is the exclusive prefix sum
    of costs in sorted order and C the total.
-4. Workers. With W_eff = min(W, C) so that no interval is empty, worker w < W_eff owns
-   the cost interval [floor(w C / W_eff), floor((w+1) C / W_eff)); workers w >= W_eff
-   are idle. Page j of item k sits at position C_k + overhead + j; the worker owning
-   that position processes the page. So each worker gets a contiguous run of (item, page) pairs,
-   stored as begin (item, page) inclusive and end (item, page) exclusive.
+4. Workers. The item's overhead is spread evenly over its pages: page j of item k starts
+   at the cost position x = C_k + j * c_k / pages_k (a rational number), so a batch of
+   equal items cuts into equal page counts whatever the overhead. W_eff =
+   min(W, floor(2 C / (2 + overhead))) workers are used; that keeps each worker's
+   interval at least as long as one page of any item of two or more pages, so no
+   worker inside a split item's range is left without pages. Worker w < W_eff owns the
+   pages whose start lies in [w C / W_eff, (w+1) C / W_eff), i.e. worker
+   floor(x W_eff / C); workers w >= W_eff are idle. So each worker gets a contiguous
+   run of (item, page) pairs, stored as begin (item, page) inclusive and end (item,
+   page) exclusive.
 5. Splits. An item whose pages span several workers is split; ``owner`` is the worker of
    its page 0, ``nsplits`` the number of workers it spans, and its partial results go to
    workspace slots slot_base .. slot_base + nsplits - 1 (split index = worker - owner).
@@ -76,9 +81,16 @@ def items_of(seqlens, s_q: int, h: int, causal: bool):
     return n_tiles, out
 
 
-def worker_of(x: int, total: int, W: int) -> int:
-    """The worker whose interval [floor(wC/W), floor((w+1)C/W)) holds position x."""
-    return ((x + 1) * W - 1) // total
+def active_workers(total: int, W: int, overhead: int) -> int:
+    """W_eff = min(W, floor(2 C / (2 + overhead)))."""
+    return min(int(W), (2 * int(total)) // (2 + int(overhead)))
+
+
+def page_worker(cost_begin: int, pages: int, j: int, overhead: int, total: int, W: int) -> int:
+    """floor(x W / C) for the start x = C_k + j (overhead + pages) / pages of page j, in
+    integers: floor((C_k pages + j (overhead + pages)) W / (C pages))."""
+    num = (int(cost_begin) * int(pages) + int(j) * (int(overhead) + int(pages))) * int(W)
+    return num // (int(total) * int(pages))
 
 
 def split_plan(seqlens, s_q: int, h: int, causal: bool, num_workers: int, overhead: int) -> Plan:
@@ -93,12 +105,12 @@ def split_plan(seqlens, s_q: int, h: int, causal: bool, num_workers: int, overhe
         cost_begin[k] = acc
         acc += overhead + it[3]
     total = acc
-    W = min(W_all, total)
+    W = active_workers(total, W_all, overhead)
     owner = np.zeros(n, dtype=np.int64)
     nsplits = np.zeros(n, dtype=np.int64)
     for k, it in enumerate(srt):
-        first = worker_of(int(cost_begin[k]) + overhead, total, W)
-        last = worker_of(int(cost_begin[k]) + overhead + it[3] - 1, total, W)
+        first = page_worker(cost_begin[k], it[3], 0, overhead, total, W)
+        last = page_worker(cost_begin[k], it[3], it[3] - 1, overhead, total, W)
         owner[k] = first
         nsplits[k] = last - first + 1
     slot_base = np.full(n, -1, dtype=np.int64)
@@ -113,11 +125,15 @@ def split_plan(seqlens, s_q: int, h: int, causal: bool, num_workers: int, overhe
     we = np.zeros((W_all, 2), dtype=np.int64)
 
     def start_of(w):
+        """First page (in order) whose start position is >= w C / W_eff."""
         if w >= W:
             return (n, 0)
-        b = (w * total) // W
-        k = int(np.searchsorted(cost_begin, b, side="right")) - 1
-        return (k, max(0, b - int(cost_begin[k]) - overhead))
+        k = int(np.searchsorted(cost_begin * W, w * total, side="right")) - 1
+        c_k = overhead + srt[k][3]
+        # smallest j with C_k + j c_k / pages_k >= w C / W_eff
+        num = (w * total - int(cost_begin[k]) * W) * srt[k][3]
+        j = -(-num // (W * c_k))
+        return (k, j) if j < srt[k][3] else (k + 1, 0)
 
     for w in range(W_all):
         wb[w] = start_of(w)

@@ -1,5 +1,7 @@
 """Pins for the split-plan definition (CPU only): brute force over cost positions, exact
 coverage, sort order and balance bounds."""
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -15,13 +17,12 @@ CASES = [
 ]
 
 
-def _brute_worker_of_positions(total, W):
-    """Assign every cost position to a worker by walking the interval boundaries."""
-    bounds = [(w * total) // W for w in range(W)] + [total]
-    owner = np.empty(total, dtype=np.int64)
+def _brute_worker_of_position(x, total, W):
+    """Walk the interval boundaries w C / W (exact fractions) to the one holding x."""
     for w in range(W):
-        owner[bounds[w]:bounds[w + 1]] = w
-    return owner
+        if Fraction(w * total, W) <= x < Fraction((w + 1) * total, W):
+            return w
+    raise AssertionError("position outside [0, C)")
 
 
 @pytest.mark.parametrize("case", CASES)
@@ -29,7 +30,7 @@ def _brute_worker_of_positions(total, W):
 def test_plan_covers_every_page_exactly_once_by_brute_force(case, overhead):
     p = op.split_plan(case["seqlens"], case["s_q"], case["h"], case["causal"], case["W"], overhead)
     W = case["W"]
-    pos_owner = _brute_worker_of_positions(p.total_cost, min(W, p.total_cost))
+    assert p.active_workers == min(W, 2 * p.total_cost // (2 + overhead))
     seen = {}
     for w in range(W):
         for (k, lo, hi) in op.worker_segments(p, w):
@@ -37,13 +38,17 @@ def test_plan_covers_every_page_exactly_once_by_brute_force(case, overhead):
                 assert (k, j) not in seen
                 seen[(k, j)] = w
     for k in range(len(p.pages)):
-        for j in range(int(p.pages[k])):
-            x = int(p.cost_begin[k]) + overhead + j
-            assert seen[(k, j)] == pos_owner[x]
-            assert op.worker_of(x, p.total_cost, p.active_workers) == pos_owner[x]
-        owners = {seen[(k, j)] for j in range(int(p.pages[k]))}
+        pk = int(p.pages[k])
+        for j in range(pk):
+            # page j starts at C_k + j (overhead + pages) / pages
+            x = int(p.cost_begin[k]) + Fraction(j * (overhead + pk), pk)
+            w = _brute_worker_of_position(x, p.total_cost, p.active_workers)
+            assert seen[(k, j)] == w
+            assert op.page_worker(p.cost_begin[k], pk, j, overhead, p.total_cost, p.active_workers) == w
+        owners = {seen[(k, j)] for j in range(pk)}
         assert int(p.owner[k]) == min(owners)
         assert int(p.nsplits[k]) == len(owners)
+        # every worker inside a split item's range has pages of it
         assert owners == set(range(min(owners), max(owners) + 1))
     assert len(seen) == int(np.sum(p.pages))
 
@@ -86,8 +91,23 @@ def test_plan_slots_and_balance(case):
     assert slots == list(range(p.n_slots))
 
 
-def test_uniform_batch_splits_evenly_without_overhead():
-    p = op.split_plan([4096] * 64, 1, 128, False, 256, 0)
+@pytest.mark.parametrize("overhead", [0, 2, 5])
+def test_uniform_batch_splits_evenly_whatever_the_overhead(overhead):
+    """Equal items: each page costs the same, so 64 items of 64 pages cut into 16 pages per
+    worker, 4 parts per item, for any overhead."""
+    p = op.split_plan([4096] * 64, 1, 128, False, 256, overhead)
     assert all(n == 4 for n in p.nsplits)
+    assert list(p.owner) == [4 * k for k in range(64)]
     per_worker = [sum(hi - lo for (_, lo, hi) in op.worker_segments(p, w)) for w in range(256)]
     assert set(per_worker) == {16}
+
+
+def test_tiny_batch_uses_fewer_workers_than_cost_units():
+    """Two items of 4 pages, overhead 2: C = 12, W_eff = floor(24 / 4) = 6; pages start at
+    0, 1.5, 3, 4.5 and 6, 7.5, 9, 10.5; intervals of length 2."""
+    p = op.split_plan([256, 256], 1, 16, False, 256, 2)
+    assert p.total_cost == 12 and p.active_workers == 6
+    segs = [op.worker_segments(p, w) for w in range(8)]
+    assert segs[:6] == [[(0, 0, 2)], [(0, 2, 3)], [(0, 3, 4)], [(1, 0, 2)], [(1, 2, 3)], [(1, 3, 4)]]
+    assert segs[6:] == [[], []]
+    assert list(p.owner) == [0, 3] and list(p.nsplits) == [3, 3]
