@@ -642,9 +642,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const int32_t* __
   const int n_split = plan[kHSplitItems];
   const int n_items = plan[kHItems];
   if ((int)blockIdx.x >= n_split) return;
-  const int k = plan[plan_split_off(n_items, plan[kHWorkers]) + blockIdx.x];
-  const int32_t* it = plan + plan_items_off() + kItemWords * k;
-  const int seq = it[kISeq], tile = it[kITile], ns_all = it[kINsplits], slot0 = it[kISlot];
+  const int32_t* sr = plan + plan_split_off(n_items, plan[kHWorkers]) + kSplitWords * blockIdx.x;
+  const int seq = sr[kSSeq], tile = sr[kSTile], ns_all = sr[kSNsplits], slot0 = sr[kSSlot];
   const int rows_total = s_q * heads;
   const int nt = blockIdx.y;
   if (kRowsPerTile * tile + 32 * nt >= rows_total) return;

@@ -158,7 +158,8 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int worker = xcd_worker();
-  if (plan[kHMagic] != kPlanMagic || plan[kHWorkers] != (int)gridDim.x || plan[kHBatch] != a.batch ||
+  if (plan[kHMagic] != kPlanMagic || plan[kHVersion] != kPlanVersion || plan[kHWorkers] != (int)gridDim.x ||
+      plan[kHBatch] != a.batch ||
       plan[kHSq] != a.s_q || plan[kHHeads] != a.heads || plan[kHCausal] != a.causal)
     return;
   const int n_items = plan[kHItems];
@@ -219,17 +220,44 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
 #pragma unroll
     for (int n = 0; n < kR32Dma; ++n) tab[64 * 4 * n] = dma_voff32(wave, n, lane);
   }
-  // the first step, then the first item's query rows, then two more steps: the first scores
-  // wait only for the first step and the queries
-#pragma unroll 1
-  for (int i = 0; i < kR32Slots - 1; ++i) {   // (zero-record loads past the worker's range)
+  // one step of the load cursor into the ring (zero-record loads past the worker's range)
+  auto issue_step = [&]() {
     const i32x4 rs = lc.k <= k_last ? cursor_rsrc<false>(lc, a, kv_ptr, nullptr).kv
                                     : make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
 #pragma unroll
     for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + load_slot * kBufBytes, n, offtab[64 * 4 * n], wave);
     advance();
-    if (i == 0) load_q(kb);
+  };
+  // Start-up: the first item's 128 query rows (147 KB, contiguous in q) are staged through
+  // the four ring slots by LDS-DMA, 32 rows per slot in the cache-step layout, and each wave
+  // reads its 32 rows back with the score-operand read pattern. (Loaded straight into
+  // registers, each load instruction would touch 32 rows; with every worker starting at
+  // once, that burst is bound by the number of cache lines.) Rows past the last query row
+  // read as zeros. Then the first ring steps.
+  {
+    const int32_t* it = plan + plan_items_off() + kItemWords * kb;
+    const int tile0 = kRowsPerTile * it[kITile];
+    const int valid_rows = rows_total - tile0 < kRowsPerTile ? rows_total - tile0 : kRowsPerTile;
+    const uint64_t qbase = reinterpret_cast<uint64_t>(q_ptr) +
+                           ((uint64_t)it[kISeq] * (uint64_t)rows_total + (uint64_t)tile0) * kRowBytes;
+#pragma unroll 1
+    for (int sl = 0; sl < kR32Slots; ++sl) {
+      int bytes = valid_rows * kRowBytes - sl * kBufBytes;
+      bytes = bytes < 0 ? 0 : (bytes > kBufBytes ? kBufBytes : bytes);
+      const i32x4 rs = make_rsrc(qbase + (uint64_t)sl * kBufBytes, bytes);
+#pragma unroll
+      for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + sl * kBufBytes, n, offtab[64 * 4 * n], wave);
+    }
+    wait_vmcnt<0>();
+    barrier_lds();
+    const QkAddr qa = qk_addr((uint32_t)wave * kBufBytes, lane);
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) qreg[ks] = lds_b128(lds + (qa.b[ks & 3] + 128 * (ks >> 2)));
+    q_item = kb;
+    barrier_lds();   // every wave holds its rows before the ring is refilled
   }
+#pragma unroll 1
+  for (int i = 0; i < kR32Slots - 1; ++i) issue_step();
 
   int comp_slot = 0;   // ring slot of the segment's current step
 
@@ -238,19 +266,27 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     const Seg sg = seg_of(plan, k, kb, pb, ke, pe);
     const int32_t* it = plan + plan_items_off() + kItemWords * k;
 
-    // ---- keys visible to this lane's query row 32*wave + l%32
+    // ---- keys visible to this lane's query row 32*wave + l%32, from the item's visible count
+    // (that of its last row; the plan holds it, so no length load sits on the item's start):
+    // row j of a causal tile sees j_last - j keys fewer; lengths above the block table's
+    // capacity read as that capacity
     int lim = 0;
     {
-      const int g_row = kRowsPerTile * it[kITile] + 32 * wave + (lane & 31);
+      const int tile_row0 = kRowsPerTile * it[kITile];
+      const int g_row = tile_row0 + 32 * wave + (lane & 31);
       if (g_row < rows_total) {
-        int t = seqlens[it[kISeq]];
-        t = t < 0 ? 0 : t;
+        const int vis = it[kIVis];
         const int cap = a.max_pages * kPage;
-        t = t > cap ? cap : t;
-        lim = t;
         if (a.causal) {
-          lim = t - a.s_q + 1 + g_row / a.heads;
-          lim = lim < 0 ? 0 : (lim > t ? t : lim);
+          const int last_row = (tile_row0 + kRowsPerTile < rows_total ? tile_row0 + kRowsPerTile : rows_total) - 1;
+          const int jt = g_row / a.heads, jt_last = last_row / a.heads;
+          int lv = vis > 0 ? vis - (jt_last - jt) : 0;
+          lv = lv < 0 ? 0 : lv;
+          int lc = cap - a.s_q + 1 + jt;
+          lc = lc < 0 ? 0 : lc;
+          lim = lv < lc ? lv : lc;
+        } else {
+          lim = vis < cap ? vis : cap;
         }
       }
     }
@@ -463,13 +499,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       load_slot = 0;
       comp_slot = 0;
 #pragma unroll 1
-      for (int j = 0; j < kR32Slots - 1; ++j) {
-        const i32x4 rs = lc.k <= k_last ? cursor_rsrc<false>(lc, a, kv_ptr, nullptr).kv
-                                        : make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
-#pragma unroll
-        for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + load_slot * kBufBytes, n, offtab[64 * 4 * n], wave);
-        advance();
-      }
+      for (int j = 0; j < kR32Slots - 1; ++j) issue_step();
     }
 
     // ---- finalize (wave-local): out = O / l and lse = m + log2(l), or, for items the plan
@@ -564,20 +594,20 @@ constexpr int kCmbBatch = 4;         // parts whose data is in flight together
 __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32_t* __restrict__ plan,
                                                                      const char* __restrict__ ws,
                                                                      float* __restrict__ out,
-                                                                     float* __restrict__ lse, int s_q, int heads) {
+                                                                     float* __restrict__ lse, int s_q, int heads,
+                                                                     int n_items, int workers) {
   __shared__ __attribute__((aligned(16))) float wts[kCmbMaxSplits][32];   // [part][row]: m_k, then weights
   __shared__ float dens[kCmbMaxSplits][32];                               // [part][row]: l_k
   __shared__ float tile_out[32][128 + 4];
   __shared__ __attribute__((aligned(16))) float row_resc[32];
   __shared__ __attribute__((aligned(16))) float row_t[32];
   __shared__ float row_m[32];
-  if (plan[kHMagic] != kPlanMagic) return;
-  const int n_split = plan[kHSplitItems];
-  const int n_items = plan[kHItems];
-  if ((int)blockIdx.x >= n_split) return;
-  const int k = plan[plan_split_off(n_items, plan[kHWorkers]) + blockIdx.x];
-  const int32_t* it = plan + plan_items_off() + kItemWords * k;
-  const int seq = it[kISeq], tile = it[kITile], ns_all = it[kINsplits], slot0 = it[kISlot];
+  // the header and this block's split record in one round trip (the record area holds
+  // n_items entries, so the read is in bounds for every block of the grid)
+  const int32_t* sr = plan + plan_split_off(n_items, workers) + kSplitWords * blockIdx.x;
+  const int magic = plan[kHMagic], n_split = plan[kHSplitItems];
+  const int seq = sr[kSSeq], tile = sr[kSTile], ns_all = sr[kSNsplits], slot0 = sr[kSSlot];
+  if (magic != kPlanMagic || (int)blockIdx.x >= n_split) return;
   const int rows_total = s_q * heads;
   const int w = blockIdx.y, cq = blockIdx.z;
   if (kRowsPerTile * tile + 32 * w >= rows_total) return;
@@ -711,9 +741,10 @@ hipError_t launch_decode_rows32(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream) {
-  const int max_split = a.workers;   // split items <= active workers - 1
+  const int n_items = a.batch * tiles_per_seq(a.s_q, a.heads);
+  const int max_split = a.workers < n_items ? a.workers : n_items;   // split items <= both
   hipLaunchKernelGGL(combine_rows32_kernel, dim3(max_split, kRowsPerTile / 32, 4), dim3(kCmbThreads), 0, stream,
-                     a.plan, reinterpret_cast<const char*>(a.ws), a.out, a.lse, a.s_q, a.heads);
+                     a.plan, reinterpret_cast<const char*>(a.ws), a.out, a.lse, a.s_q, a.heads, n_items, a.workers);
   return hipGetLastError();
 }
 

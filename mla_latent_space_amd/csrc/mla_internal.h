@@ -31,6 +31,10 @@ constexpr int kItemWords = 8;
 enum ItemField { kISeq = 0, kITile, kIVis, kIPages, kICost, kIOwner, kINsplits, kISlot };
 // worker record: item_begin, page_begin, item_end, page_end (end exclusive)
 constexpr int kWorkerWords = 4;
+// split record (one per split item, in sorted order): seq, tile, nsplits, slot_base
+constexpr int kSplitWords = 4;
+enum SplitField { kSSeq = 0, kSTile, kSNsplits, kSSlot };
+constexpr int kPlanVersion = 2;
 
 __host__ __device__ inline int plan_items_off() { return kHeaderWords; }
 __host__ __device__ inline int plan_workers_off(int n_items) { return kHeaderWords + kItemWords * n_items; }
@@ -38,7 +42,7 @@ __host__ __device__ inline int plan_split_off(int n_items, int workers) {
   return plan_workers_off(n_items) + kWorkerWords * workers;
 }
 __host__ __device__ inline int64_t plan_words(int n_items, int workers) {
-  return (int64_t)plan_split_off(n_items, workers) + n_items;
+  return (int64_t)plan_split_off(n_items, workers) + (int64_t)kSplitWords * n_items;
 }
 __host__ __device__ inline int tiles_per_seq(int s_q, int heads) {
   return (s_q * heads + kRowsPerTile - 1) / kRowsPerTile;

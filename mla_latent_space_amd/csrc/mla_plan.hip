@@ -224,7 +224,13 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     it[kIOwner] = first;
     it[kINsplits] = ns;
     it[kISlot] = ns > 1 ? (pack_run >> 16) : -1;
-    if (ns > 1) split_list[pack_run & 0xFFFF] = k;
+    if (ns > 1) {
+      int32_t* sr = split_list + kSplitWords * (pack_run & 0xFFFF);
+      sr[kSSeq] = sq;
+      sr[kSTile] = tl;
+      sr[kSNsplits] = ns;
+      sr[kSSlot] = pack_run >> 16;
+    }
     pack_run += ns > 1 ? ((ns << 16) | 1) : 0;
   }
   // workers: start(w) = the first page whose start position is >= w C / Weff
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
   }
   if (tid == 0) {
     plan[kHMagic] = kPlanMagic;
-    plan[kHVersion] = 1;
+    plan[kHVersion] = kPlanVersion;
     plan[kHBatch] = batch;
     plan[kHSq] = s_q;
     plan[kHHeads] = heads;

@@ -39,8 +39,8 @@ def test_version_and_status_strings():
 def test_sizes():
     # 64 items (one 128-row tile each), 256 workers
     n, W = 64, 256
-    assert mla.plan_bytes(64, 1, 128, W) == 4 * (16 + 8 * n + 4 * W + n)
-    assert mla.plan_bytes(32, 16, 128, W) == 4 * (16 + 9 * 32 * 16 + 4 * W)
+    assert mla.plan_bytes(64, 1, 128, W) == 4 * (16 + 8 * n + 4 * W + 4 * n)
+    assert mla.plan_bytes(32, 16, 128, W) == 4 * (16 + 12 * 32 * 16 + 4 * W)
     # per split part: 128 x 512 bf16 partial out + 128 fp32 lse
     assert mla.workspace_bytes(64, 1, 128, W) == 2 * (W - 1) * (128 * 512 * 2 + 128 * 8)
     assert mla.workspace_bytes(64, 1, 128, 1) == 0

@@ -51,11 +51,13 @@ def _check_sampled(w, seqs, num_workers=None):
 def _plan_words(p: op.Plan, batch, s_q, heads, causal):
     n = len(p.pages)
     W = p.num_workers
-    hdr = [0x4D4C4150, 1, batch, s_q, heads, int(causal), W, p.n_tiles, n, p.overhead, p.total_cost,
+    hdr = [0x4D4C4150, 2, batch, s_q, heads, int(causal), W, p.n_tiles, n, p.overhead, p.total_cost,
            p.active_workers, len(p.split_items), p.n_slots, 0, 0]
     items = np.stack([p.seq, p.tile, p.vis, p.pages, p.cost_begin, p.owner, p.nsplits, p.slot_base], axis=1)
     workers = np.concatenate([p.worker_begin, p.worker_end], axis=1)
-    return np.array(hdr, dtype=np.int64), items.astype(np.int64), workers.astype(np.int64), p.split_items
+    k = p.split_items
+    split = np.stack([p.seq[k], p.tile[k], p.nsplits[k], p.slot_base[k]], axis=1).reshape(-1)
+    return np.array(hdr, dtype=np.int64), items.astype(np.int64), workers.astype(np.int64), split.astype(np.int64)
 
 
 PLAN_CASES = [
@@ -214,6 +216,21 @@ def test_page_ids_out_of_range_read_as_zeros():
     bt0[0, 1] = w.num_pages
     ro, rl = om.decode_latent(w.q, kv0, None, "bf16", bt0, w.seqlens, w.scale, False)
     compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, BF16_TOL, "oob")
+
+
+@pytest.mark.parametrize("s_q,causal", [(1, False), (4, True)])
+def test_lengths_beyond_block_table_capacity(s_q, causal):
+    """A length above max_pages * 64 reads as max_pages * 64 (the documented cap): same result
+    as the oracle run at the capped length."""
+    w = wl.make_workload("cap", batch=2, s_q=s_q, heads=32, seqlens=[150, 70], causal=causal, seed=28,
+                         poison=False)
+    cap = w.block_table.shape[1] * 64
+    capped = wl.Workload(**{**w.__dict__, "seqlens": np.array([cap, 70], dtype=w.seqlens.dtype)})
+    beyond = wl.Workload(**{**w.__dict__, "seqlens": np.array([cap + 40, 70], dtype=w.seqlens.dtype)})
+    _say("lengths beyond capacity", s_q, causal)
+    out, lse = Dev(beyond).run(5)
+    ro, rl = _oracle_all(capped)
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, BF16_TOL, f"beyond capacity s_q={s_q}")
 
 
 # ----------------------------------------------------------------------------- full-size workloads
