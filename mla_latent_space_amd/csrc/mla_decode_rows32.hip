@@ -271,6 +271,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     // row j of a causal tile sees j_last - j keys fewer; lengths above the block table's
     // capacity read as that capacity
     int lim = 0;
+    int lim_min;   // smallest count over the wave's valid rows: steps below it need no mask
     {
       const int tile_row0 = kRowsPerTile * it[kITile];
       const int g_row = tile_row0 + 32 * wave + (lane & 31);
@@ -289,6 +290,13 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
           lim = vis < cap ? vis : cap;
         }
       }
+      int m = g_row < rows_total ? lim : 0x7FFFFFFF;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_xor(m, d, 64);
+        m = y < m ? y : m;
+      }
+      lim_min = __builtin_amdgcn_readfirstlane(m);
     }
     if (q_item != k) load_q(k);   // (after an item with no steps)
 
@@ -320,35 +328,45 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     // maximum as the reference. Pieces: 0 waits for the scores, 1..4 take the max, 5 masks
     // (a masked step only) and updates the reference, 6..21 exponentiate one value each and
     // round P to bf16, 22 sums.
-    float sm_mx, sm_muse, sm_psum;
+    // The row maximum is taken only where it is needed: on the segment's first step (which
+    // sets the reference of every row that sees a key in the segment), on masked steps, and
+    // on every step of a tracking pass. Elsewhere the only guard is the row sum: it bounds
+    // every P, and the pass ends with a check that it stayed below 2^60.
+    float sm_mx, sm_muse = 0.f, sm_psum;
+    bool sm_do_max = true, sm_masked = false, track = false;
     auto softmax_piece = [&](f32x16& s, int hh, bool live, int piece, bf16x8* pk) {
       if (piece == 0) {
         mfma_result_wait(s);
+        sm_masked = kStep * (hh + 1) > lim_min;   // (wave-uniform)
+        sm_do_max = track || sm_masked || hh == sg.hh0;
       } else if (piece <= 4) {
-        const int r0 = 4 * (piece - 1);
-        float mx = piece == 1 ? -INFINITY : sm_mx;
+        if (sm_do_max) {
+          const int r0 = 4 * (piece - 1);
+          float mx = piece == 1 ? -INFINITY : sm_mx;
 #pragma unroll
-        for (int r = r0; r < r0 + 4; ++r) mx = fmaxf(mx, s[r]);
-        sm_mx = mx;
-      } else if (piece == 5) {
-        const int key_end = kStep * (hh + 1);
-        if (__ballot(key_end > lim) != 0) {   // a masked step (the sequence's last, or causal rows)
-          const int key0 = kStep * hh + 4 * (lane >> 5);
-          float mx = -INFINITY;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[r] = (key0 + 8 * (r >> 2) + (r & 3)) < lim ? s[r] : -INFINITY;
-            mx = fmaxf(mx, s[r]);
-          }
+          for (int r = r0; r < r0 + 4; ++r) mx = fmaxf(mx, s[r]);
           sm_mx = mx;
         }
-        const float mx = max_across_halves(sm_mx) * a.scale_log2;
-        if (live) {
-          m_seen = fmaxf(m_seen, mx);
-          m_run = (m_run == -INFINITY && mx != -INFINITY) ? ceilf(mx) : m_run;
-          window_exceeded = window_exceeded || mx > m_run + kWindow;
+      } else if (piece == 5) {
+        if (sm_do_max) {
+          if (sm_masked) {   // the sequence's last step, or causal rows
+            const int key0 = kStep * hh + 4 * (lane >> 5);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              s[r] = (key0 + 8 * (r >> 2) + (r & 3)) < lim ? s[r] : -INFINITY;
+              mx = fmaxf(mx, s[r]);
+            }
+            sm_mx = mx;
+          }
+          const float mx = max_across_halves(sm_mx) * a.scale_log2;
+          if (live) {
+            m_seen = fmaxf(m_seen, mx);
+            m_run = (m_run == -INFINITY && mx != -INFINITY) ? ceilf(mx) : m_run;
+            window_exceeded = window_exceeded || (track && mx > m_run + kWindow);
+          }
+          sm_muse = (m_run == -INFINITY) ? 0.f : m_run;
         }
-        sm_muse = (m_run == -INFINITY) ? 0.f : m_run;
         sm_psum = 0.f;
       } else if (piece <= 21) {
         const int r = piece - 6;
@@ -363,7 +381,8 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     constexpr int kPieces = 23;
 
 #pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < 3; ++pass) {
+      track = pass > 0;
 #pragma unroll
       for (int c = 0; c < 16; ++c) o[c] = f32x16{};
       if (nsteps > 0) {
@@ -478,19 +497,30 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       {
         int32_t __attribute__((address_space(3)))* vote =
             (int32_t __attribute__((address_space(3)))*)(lds + kR32LdsBytes + 512);
-        const bool wave_exceeded = __ballot(window_exceeded) != 0;   // (all lanes take part)
+        // (a NaN sum counts as out of range)
+        const bool lane_bad = track ? window_exceeded : !(l_run <= 0x1p60f);
+        const bool wave_exceeded = __ballot(lane_bad) != 0;   // (all lanes take part)
         if (lane == 0) vote[wave] = wave_exceeded ? 1 : 0;
         barrier_lds();
         const bool again = (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
         barrier_lds();   // (the votes are read before the area is reused)
-        if (!again || pass == 1) break;
+        if (!again || pass == 2) break;
       }
-      // Second pass over the segment: every row takes the segment's maximum as its reference,
-      // so no P exceeds 1. Wait for the loads in flight (the next item's first steps), then
-      // restart the load cursor at the segment's first step in an empty ring.
+      // Another pass over the segment. After the first: every row takes m + log2(l) rounded
+      // up, which is at least its maximum, so no P exceeds 1; a row whose sum overflowed takes
+      // its reference afresh, and the pass takes the maximum on every step with the window
+      // check. After that (a tracking pass that left the window): the segment's maximum.
+      // Wait for the loads in flight (the next item's first steps), then restart the load
+      // cursor at the segment's first step in an empty ring.
       wait_vmcnt<0>();
       barrier_lds();
-      m_run = (m_seen == -INFINITY) ? -INFINITY : ceilf(m_seen);
+      if (pass == 0) {
+        const bool ok = m_run != -INFINITY && l_run > 0.f && l_run <= 0x1p126f;
+        m_run = ok ? ceilf(m_run + __log2f(l_run)) : -INFINITY;
+      } else {
+        m_run = (m_seen == -INFINITY) ? -INFINITY : ceilf(m_seen);
+      }
+      m_seen = -INFINITY;
       l_run = 0.f;
       window_exceeded = false;
       cursor_enter(lc, plan, k, kb, pb, ke, pe);

@@ -149,9 +149,9 @@ def _bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 @pytest.mark.parametrize("W", [1, 5, 256])
 def test_scores_growing_past_the_reference_window(W):
-    """Scores that grow along the sequence by hundreds of log2 units: a row's maximum leaves
-    the window above its first-step reference, so the kernel must take its second pass over
-    the segment with the segment's maximum as the reference (else P overflows)."""
+    """Scores that grow along the sequence by hundreds of log2 units: the first pass's row
+    sum overflows, so the kernel redoes the segment taking the row maximum on every step,
+    then (a row still leaving the window) with the segment's maximum as the reference."""
     w = wl.make_workload("ramp", batch=2, s_q=1, heads=32, seqlens=[600, 3000], seed=31, poison=False)
     q = _bits_to_f32(w.q)
     q[:, :, :16, :64] = 64.0            # heads 0..15 align with the ramp direction
@@ -168,6 +168,29 @@ def test_scores_growing_past_the_reference_window(W):
     out, lse = d.run(W)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, BF16_TOL, f"ramp W={W}")
+
+
+def test_scores_growing_moderately_past_the_reference_window():
+    """Heads 0..15 score exactly 90 j / (t - 1) log2 units at token j (one query channel of
+    864 against a cached channel that ramps from 0 to 1): the row maximum ends about 87 log2
+    units above the first-step reference, so the first pass's row sum is finite but above
+    2^60, and the segment is redone with the reference ceil(m + log2 l)."""
+    w = wl.make_workload("ramp90", batch=2, s_q=1, heads=32, seqlens=[600, 3000], seed=32, poison=False)
+    q = _bits_to_f32(w.q)
+    q[:, :, :16, :] = 0.0
+    q[:, :, :16, 0] = 864.0
+    w.q = _bf16_bits(q)
+    kv = _bits_to_f32(w.kv)
+    for b, t in enumerate(w.seqlens):
+        for j in range(t):
+            kv[w.block_table[b, j // 64], j % 64, 0] = j / (t - 1)
+    w.kv = _bf16_bits(kv)
+    _say("ramp 90")
+    ro, rl = _oracle_all(w)
+    d = Dev(w)
+    out, lse = d.run(1)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, BF16_TOL, "ramp 90")
 
 
 def test_plan_independence_and_bitwise_repeat():
