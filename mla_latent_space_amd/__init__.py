@@ -106,8 +106,10 @@ class SplitPlan:
 
 
 def get_split_plan(seqlens: torch.Tensor, s_q: int, heads: int, causal: bool = False,
-                   num_workers: Optional[int] = None) -> SplitPlan:
-    """Enqueue the split-KV planner on the current stream (see mla_get_split_plan)."""
+                   num_workers: Optional[int] = None, out: Optional[torch.Tensor] = None) -> SplitPlan:
+    """Enqueue the split-KV planner on the current stream (see mla_get_split_plan). `out`, a
+    contiguous uint8 CUDA tensor of at least plan_bytes(...) bytes, is written in place of a
+    new buffer (no allocation: usable under graph capture)."""
     if seqlens.dtype != torch.int32 or not seqlens.is_cuda or not seqlens.is_contiguous():
         raise ValueError("seqlens must be a contiguous int32 CUDA tensor")
     batch = seqlens.numel()
@@ -115,7 +117,12 @@ def get_split_plan(seqlens: torch.Tensor, s_q: int, heads: int, causal: bool = F
     nbytes = plan_bytes(batch, s_q, heads, W)
     if nbytes == 0:
         _check(int(lib().mla_get_split_plan(None, batch, s_q, heads, int(causal), W, None, 0, None)))
-    buf = torch.empty(nbytes, dtype=torch.uint8, device=seqlens.device)
+    if out is not None:
+        if out.dtype != torch.uint8 or not out.is_cuda or not out.is_contiguous() or out.numel() < nbytes:
+            raise ValueError(f"out must be a contiguous uint8 CUDA tensor of at least {nbytes} bytes")
+        buf = out
+    else:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=seqlens.device)
     _check(int(lib().mla_get_split_plan(seqlens.data_ptr(), batch, s_q, heads, int(causal), W, buf.data_ptr(),
                                         nbytes, _stream(seqlens))))
     return SplitPlan(buf, batch, s_q, heads, bool(causal), W)

@@ -256,6 +256,49 @@ def test_lengths_beyond_block_table_capacity(s_q, causal):
     compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, BF16_TOL, f"beyond capacity s_q={s_q}")
 
 
+def test_graph_capture_replays_match_eager():
+    """The plan and decode calls allocate nothing (given their buffers) and never wait on the
+    host, so a whole step can be captured in a HIP graph. Every replay, with eager work on the
+    same buffers between replays, must equal the eager step bit for bit."""
+    w = wl.make_workload("graph", batch=6, s_q=1, heads=128, seqlens=[5000, 64, 700, 1, 2049, 3000], seed=33)
+    d = Dev(w)
+    W = 64
+    plan_buf = torch.empty(mla.plan_bytes(w.batch, w.s_q, w.heads, W), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(16, mla.workspace_bytes(w.batch, w.s_q, w.heads, W)), dtype=torch.uint8, device="cuda")
+    out = torch.empty(w.batch, w.s_q, w.heads, 512, dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.batch, w.s_q, w.heads, dtype=torch.float32, device="cuda")
+
+    def step():
+        plan = mla.get_split_plan(d.sl, w.s_q, w.heads, w.causal, W, out=plan_buf)
+        mla.decode_fwd(d.q, d.kv, d.bt, d.sl, w.scale, kv_scales=d.scales, causal=w.causal, plan=plan,
+                       workspace=ws, out=out, lse=lse)
+
+    _say("graph capture")
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    ro, rl = _oracle_all(w)
+    compare(ref_out.cpu().numpy(), ref_lse.cpu().numpy(), ro, rl, BF16_TOL, "graph eager step")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        out.zero_()
+        lse.zero_()
+        plan_buf.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {r} differs from the eager step"
+
+
 # ----------------------------------------------------------------------------- full-size workloads
 
 def test_dsv3_full_size_sampled():
