@@ -109,7 +109,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first (the clocks settle over the first few hundred steps)")
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--rotate", type=int, default=0, help="KV copies to cycle through (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
