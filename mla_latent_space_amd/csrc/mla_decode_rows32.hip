@@ -118,26 +118,30 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Per-lane LDS byte addresses of the operand reads of one ring slot (slot offset zoff
-// included), rebuilt from an opaque lane id at each use so that they hold no registers
-// across the step loop.
+// Per-lane LDS byte addresses of the operand reads of one ring slot: the lane's part is
+// computed once (8 VGPRs held across the loop) and the slot offset added per use; the
+// tile's part goes into the instructions' offset field.
 // scores: lane reads token l%32, logical chunk 2ks + l/32 -> b[ks % 4] + 128 (ks / 4)
 struct QkAddr { uint32_t b[4]; };
 __device__ __forceinline__ QkAddr qk_addr(uint32_t zoff, int lane) {
-  int l = lane;
-  asm volatile("" : "+v"(l));
+  const int l = lane;
   const uint32_t T = l & 31, h = l >> 5;
   QkAddr r;
 #pragma unroll
   for (int x = 0; x < 4; ++x) r.b[x] = zoff + T * kRowBytes + 16 * ((2 * x + h) ^ sw32(T));
   return r;
 }
+__device__ __forceinline__ QkAddr qk_at(const QkAddr& base, uint32_t zoff) {
+  QkAddr r;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) r.b[x] = base.b[x] + zoff;
+  return r;
+}
 // values: lane (G = l/16, j = l%16) reads token 16q + 8e + 4(G/2) + j/4, channels
 // 32c + 16(G%2) + 4(j%4) .. +3 -> b[e][c % 2] + 16q rows + 128 (c / 2)
 struct PvAddr { uint32_t b[2][2]; };
 __device__ __forceinline__ PvAddr pv_addr(uint32_t zoff, int lane) {
-  int l = lane;
-  asm volatile("" : "+v"(l));
+  const int l = lane;
   const uint32_t G = l >> 4, j = l & 15;
   PvAddr r;
 #pragma unroll
@@ -146,6 +150,14 @@ __device__ __forceinline__ PvAddr pv_addr(uint32_t zoff, int lane) {
     for (int c1 = 0; c1 < 2; ++c1)
       r.b[e][c1] = zoff + (8 * e + 4 * (G >> 1) + (j >> 2)) * kRowBytes +
                    16 * ((4 * c1 + 2 * (G & 1) + ((j >> 1) & 1)) ^ (4 * (j >> 3) + 2 * e + (G >> 1))) + 8 * (j & 1);
+  return r;
+}
+__device__ __forceinline__ PvAddr pv_at(const PvAddr& base, uint32_t zoff) {
+  PvAddr r;
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int c1 = 0; c1 < 2; ++c1) r.b[e][c1] = base.b[e][c1] + zoff;
   return r;
 }
 
@@ -169,6 +181,8 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   k_last = k_last < n_items - 1 ? k_last : n_items - 1;
   if (kb >= n_items || k_last < kb) return;
   const int rows_total = a.s_q * a.heads;
+  const QkAddr qk0 = qk_addr(0, lane);   // operand addresses in slot 0
+  const PvAddr pv0 = pv_addr(0, lane);
 
   // Q^T B operand of item k: lane holds query row 32*wave + l%32 of the item's tile, channels
   // 16ks + 8(l/32) .. +7. Rows past the last query row (a partial tile) load the sequence's
@@ -250,7 +264,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     }
     wait_vmcnt<0>();
     barrier_lds();
-    const QkAddr qa = qk_addr((uint32_t)wave * kBufBytes, lane);
+    const QkAddr qa = qk_at(qk0, (uint32_t)wave * kBufBytes);
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) qreg[ks] = lds_b128(lds + (qa.b[ks & 3] + 128 * (ks >> 2)));
     q_item = kb;
@@ -395,7 +409,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       {
         f32x16 s;
         bf16x8 qring[kR32QkRing];
-        const QkAddr qa = qk_addr(zc, lane);
+        const QkAddr qa = qk_at(qk0, zc);
 #pragma unroll
         for (int t = 0; t < kR32QkRing; ++t) qring[t] = qk_read(qa, t);
 #pragma unroll
@@ -407,7 +421,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         }
 #pragma unroll
         for (int p = 0; p < kPieces; ++p) softmax_piece(s, sg.hh0, true, p, pcur);
-        const PvAddr pa = pv_addr(zc, lane);
+        const PvAddr pa = pv_at(pv0, zc);
 #pragma unroll
         for (int t = 0; t < kR32Ring; ++t) pring[t] = pv_read(pa, t);
       }
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         };
         // 1) the first value MFMAs of step i (their first operands were read before the barrier)
         {
-          const PvAddr pa = pv_addr(zc, lane);
+          const PvAddr pa = pv_at(pv0, zc);
 #pragma unroll
           for (int t = 0; t < kR32PvLead; ++t) {
             pv_mfma(pa, t, kR32PvLead);
@@ -448,10 +462,10 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         //    turns over to the next value operands during the last score MFMAs
         {
           bf16x8 qring[kR32QkRing];
-          const QkAddr qa = qk_addr(zn, lane);
+          const QkAddr qa = qk_at(qk0, zn);
 #pragma unroll
           for (int t = 0; t < kR32QkRing; ++t) qring[t] = qk_read(qa, t);
-          const PvAddr pa = pv_addr(zc, lane);
+          const PvAddr pa = pv_at(pv0, zc);
 #pragma unroll
           for (int t = 0; t < 36; ++t) {
             const bf16x8 cur = qring[t % kR32QkRing];
@@ -466,7 +480,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         }
         // 3) the remaining value MFMAs of step i, the softmax of step i+1 between them
         {
-          const PvAddr pa = pv_addr(zc, lane);
+          const PvAddr pa = pv_at(pv0, zc);
 #pragma unroll
           for (int t = kR32PvLead; t < 32; ++t) {
             pv_mfma(pa, t, 32);
@@ -480,7 +494,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         pcur[1] = pnext[1];
         // the first value operands of step i+1 (its rows were published at the last barrier)
         {
-          const PvAddr pa = pv_addr(zn, lane);
+          const PvAddr pa = pv_at(pv0, zn);
 #pragma unroll
           for (int t = 0; t < kR32Ring; ++t) pring[t] = pv_read(pa, t);
         }
