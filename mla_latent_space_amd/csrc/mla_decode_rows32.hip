@@ -39,12 +39,11 @@ namespace {
 constexpr int kR32Threads = 256;                 // 4 waves, one per SIMD
 constexpr int kR32Slots = 4;                     // LDS ring depth (steps)
 constexpr int kR32Dma = kDmaInstr / 4;           // 9 LDS-DMA instructions per wave and step
-constexpr int kR32LdsBytes = kR32Slots * kBufBytes;   // then 4 x 32 floats of per-row 1/l, 4 votes, DMA offsets
+constexpr int kR32LdsBytes = kR32Slots * kBufBytes;   // then 4 x 32 floats of per-row 1/l, 4 votes
 constexpr int kR32PvLead = 4;                    // value MFMAs of step i before the scores of step i+1
 constexpr int kR32Ring = 4;                      // value operand reads in flight (one MFMA each)
 constexpr int kR32QkRing = 4;                    // score operand reads in flight
-constexpr int kR32OffTab = kR32LdsBytes + 512 + 16;   // DMA offset table: 36 instructions x 64 lanes
-constexpr int kR32LdsTotal = kR32OffTab + kDmaInstr * 64 * 4;
+constexpr int kR32LdsTotal = kR32LdsBytes + 512 + 16;
 static_assert(kR32LdsTotal <= 160 * 1024, "LDS budget");
 constexpr float kWindow = 64.f;                  // rows may exceed their reference max by 2^64
 static_assert(kDmaInstr % 4 == 0, "DMA split");
@@ -58,21 +57,29 @@ static_assert(32 - kR32PvLead >= 23, "softmax pieces fit between the value MFMAs
 __device__ __forceinline__ uint32_t sw32(uint32_t u) { return (((u >> 1) & 1u) << 2) | ((u >> 2) & 3u); }
 
 // Source offset (bytes from the step's first row) of LDS-DMA instruction i = wave + 4n,
-// lane l: it fills LDS chunk position p = 64i + l = 72u + pc, which holds logical chunk
-// pc ^ sw(u) of token u. floor(p / 72) and p mod 72 by full-rate 24-bit multiplies, exact
-// for p < 2304.
-__device__ __forceinline__ uint32_t dma_voff32(int wave, int n, int lane) {
-  const uint32_t p = 64u * (uint32_t)(wave + 4 * n) + (uint32_t)lane;
-  const uint32_t x = __umul24(p, 1821u);
-  const uint32_t u = x >> 17;
-  const uint32_t pc = __umul24(x & 0x1FFFFu, 72u) >> 17;
-  const uint32_t ch = (pc & ~7u) | ((pc & 7u) ^ sw32(u));
-  return __umul24(u, (uint32_t)kRowBytes) + 16u * ch;
+// lane l: it fills LDS chunk position p = 64i + l = 72u + pc (token u = floor(p / 72)),
+// which holds logical chunk pc ^ sw(u) of token u, i.e. source byte 1152u + 16 (pc ^ sw(u))
+// = 16 (p ^ sw(u)) (72u has no low bits). With p = 256n + b, b = 64 wave + l < 256, that is
+// 4096n + (16b ^ 16 sw(u)). Per lane the nine 16 sw(u) (7 bits each) are packed into three
+// words once; an instruction's offset is then one field extract and one xor-add. (All of it
+// stays in the vector offset: the buffer's range check, which zero-fills rows past the
+// visible ones, does not cover the scalar offset.)
+struct DmaOffsets { uint32_t b16, packed[3]; };
+__device__ __forceinline__ DmaOffsets dma_offsets(int wave, int lane) {
+  DmaOffsets d;
+  const uint32_t b = 64u * (uint32_t)wave + (uint32_t)lane;
+  d.b16 = 16u * b;
+  d.packed[0] = d.packed[1] = d.packed[2] = 0u;
+#pragma unroll
+  for (int n = 0; n < kDmaInstr / 4; ++n) {
+    const uint32_t u = (256u * (uint32_t)n + b) / 72u;
+    d.packed[n >> 2] |= (sw32(u) << 4) << (7 * (n & 3));
+  }
+  return d;
 }
-
-// The per-lane source offsets of a wave's 9 DMA instructions are the same for every step;
-// they are computed once into an LDS table (kept in registers they would cost 9 VGPRs,
-// recomputed they cost ~15 VALU per instruction).
+__device__ __forceinline__ uint32_t dma_voff(const DmaOffsets& d, int n) {
+  return (__builtin_amdgcn_ubfe(d.packed[n >> 2], 7 * (n & 3), 7) ^ d.b16) + 4096u * (uint32_t)n;
+}
 __device__ __forceinline__ void issue32(const i32x4& rsrc, uint32_t lds_slot, int n, uint32_t voff, int wave) {
   lds_dma_x4(lds_slot + 1024u * (uint32_t)(wave + 4 * n), voff, rsrc);
 }
@@ -225,21 +232,13 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
   };
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
-  // this wave's DMA source offsets: table entry (instruction wave + 4n, lane)
-  const uint32_t __attribute__((address_space(3)))* offtab =
-      (const uint32_t __attribute__((address_space(3)))*)(lds + kR32OffTab) + 64 * wave + lane;
-  {
-    uint32_t __attribute__((address_space(3)))* tab =
-        (uint32_t __attribute__((address_space(3)))*)(lds + kR32OffTab) + 64 * wave + lane;
-#pragma unroll
-    for (int n = 0; n < kR32Dma; ++n) tab[64 * 4 * n] = dma_voff32(wave, n, lane);
-  }
+  const DmaOffsets dmo = dma_offsets(wave, lane);   // this wave's DMA source offsets
   // one step of the load cursor into the ring (zero-record loads past the worker's range)
   auto issue_step = [&]() {
     const i32x4 rs = lc.k <= k_last ? cursor_rsrc<false>(lc, a, kv_ptr, nullptr).kv
                                     : make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
 #pragma unroll
-    for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + load_slot * kBufBytes, n, offtab[64 * 4 * n], wave);
+    for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + load_slot * kBufBytes, n, dma_voff(dmo, n), wave);
     advance();
   };
   // Start-up: the first item's 128 query rows (147 KB, contiguous in q) are staged through
@@ -260,7 +259,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       bytes = bytes < 0 ? 0 : (bytes > kBufBytes ? kBufBytes : bytes);
       const i32x4 rs = make_rsrc(qbase + (uint64_t)sl * kBufBytes, bytes);
 #pragma unroll
-      for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + sl * kBufBytes, n, offtab[64 * 4 * n], wave);
+      for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + sl * kBufBytes, n, dma_voff(dmo, n), wave);
     }
     wait_vmcnt<0>();
     barrier_lds();
@@ -473,7 +472,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
             if (t + kR32Ring >= 36) pring[t % kR32Ring] = pv_read(pa, kR32PvLead + t + kR32Ring - 36);
             if (t == 0) mfma_v0(s, cur, qreg[0]);
             else mfma_v(s, cur, qreg[t]);
-            if ((t & 3) == 0) voff = offtab[64 * 4 * (t >> 2)];   // offset of the next DMA instruction
+            if ((t & 3) == 0) voff = dma_voff(dmo, t >> 2);   // offset of the next DMA instruction
             if ((t & 3) == 3) issue32(rs, lslot, t >> 2, voff, wave);
             __builtin_amdgcn_sched_barrier(0);
           }
