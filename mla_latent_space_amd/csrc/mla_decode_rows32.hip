@@ -1,5 +1,6 @@
 // Latent-space MLA decode over a bf16 cache: one persistent work-group of four waves (one per
-// SIMD) per compute unit, each wave owning 32 query rows of the 128-row tile end to end.
+// SIMD) per compute unit; each wave owns the softmax of 32 query rows of the 128-row tile and
+// the values of a quarter of the 512 latent channels.
 //
 // Page "Mla Analysis", section "Absorption Trick (FlashMLA)": scores are Qz . Z^T with the
 // absorbed 576-wide queries and the value is the latent row itself, so one pass over the
@@ -8,26 +9,33 @@
 // MI355X bf16 ridge, so the kernel streams every cached row from HBM once per 128-row tile
 // and keeps the matrix cores busy underneath.
 //
-// Per 32-token step, per wave (rows 32w .. 32w+31):
-//  * Scores S^T[32 tokens x 32 rows] = Z Q^T: 36 v_mfma_f32_32x32x16_bf16 over the 576
-//    channels; A = Z rows from LDS (ds_read_b128), B = Q^T held in 144 VGPRs.
+// Per 32-token step, per wave w:
+//  * Scores S^T[32 tokens x 32 rows] = Z Q^T for the wave's rows 32w .. 32w+31: 36
+//    v_mfma_f32_32x32x16_bf16 over the 576 channels; A = Z rows from LDS (ds_read_b128),
+//    B = Q^T held in 144 VGPRs.
 //  * The 32x32 accumulator layout (lane: row l%32, tokens 8j + 4(l/32) + v) is, after the
 //    bf16 rounding, exactly an MFMA operand of P[32 rows x 16 tokens] when the 16 k slots
-//    of k-step q are taken as tokens 16q + 8(i/4) + 4(l/32) + i%4. So P never leaves the
-//    registers: no exchange between waves, and the softmax state of a row (reference max,
-//    sum) is lane-local (lanes l and l^32 share a row and combine with a permlane32 swap).
-//  * Values O[32 rows x 512 channels] += P Z: 32 v_mfma_f32_32x32x16_bf16, B = Z^T tiles
-//    from two ds_read_b64_tr_b16 transposing reads each; O lives in the 256 AGPRs.
+//    of k-step q are taken as tokens 16q + 8(i/4) + 4(l/32) + i%4, and the softmax state of
+//    a row (reference max, sum) is lane-local (lanes l and l^32 share a row and combine with
+//    a permlane32 swap).
+//  * Values: the wave accumulates O[all 128 rows x its 128 channels 128w ..] += P Z, 32
+//    v_mfma_f32_32x32x16_bf16 into the 256 AGPRs. A = P of each row block: the wave's own
+//    from registers, the other three waves' from a double-buffered P area in LDS (each wave
+//    writes its P there in the A-operand layout, 2 KiB per step); B = Z^T tiles of the
+//    wave's channels, two ds_read_b64_tr_b16 each. Splitting the channels rather than the
+//    rows reads each Z^T tile once per work-group instead of once per wave.
 //  * The reference max of a row is set at its first finite score and never moves, so O is
-//    never rescaled inside the loop (a rare second pass over the segment covers rows whose
-//    maximum later grows by more than 2^64).
+//    never rescaled inside the loop (a rare redo of the segment covers rows whose scores
+//    later run far above it).
 //  * LDS ring of 4 steps (36 KiB each) filled by LDS-DMA (buffer_load_dwordx4 ... lds, 9 per
-//    wave and step, source offsets from a table in LDS), rows XOR-swizzled in 16-B chunks so
-//    that both operand reads are free of bank conflicts. One barrier per step: it publishes
-//    the next step's rows and frees the slot the values of the previous step read.
-//  * Order inside a step: the first value MFMAs of step i (operands read before the
-//    barrier), the score MFMAs of step i+1 (the step's DMA instructions between them), the
-//    remaining value MFMAs of step i with the softmax of step i+1 (VALU) between them.
+//    wave and step, source offsets from three packed per-lane words), rows XOR-swizzled in
+//    16-B chunks so that both operand reads are free of bank conflicts. The ring and the two
+//    P buffers fill the 160 KiB. One barrier per step: it publishes the next step's rows and
+//    every wave's P, and frees the slot and the P buffer the previous step read.
+//  * Order inside a step: the first value MFMAs of step i (own rows, operands in registers),
+//    the score MFMAs of step i+1 (the step's DMA instructions between them), the remaining
+//    value MFMAs of step i with the softmax of step i+1 (VALU) between them, P of step i+1 to
+//    LDS.
 //  * The MFMAs are written as inline asm so that O can be pinned to AGPRs while the score
 //    accumulator stays in VGPRs; explicit waits (12+ states) precede every VALU read of an
 //    MFMA result.
@@ -39,15 +47,17 @@ namespace {
 constexpr int kR32Threads = 256;                 // 4 waves, one per SIMD
 constexpr int kR32Slots = 4;                     // LDS ring depth (steps)
 constexpr int kR32Dma = kDmaInstr / 4;           // 9 LDS-DMA instructions per wave and step
-constexpr int kR32LdsBytes = kR32Slots * kBufBytes;   // then 4 x 32 floats of per-row 1/l, 4 votes
+constexpr int kR32LdsBytes = kR32Slots * kBufBytes;   // the ring; then two P buffers
+constexpr int kR32PBytes = kRowsPerTile * kStep * 2;  // P of one step: 128 rows x 32 tokens, bf16
+constexpr int kR32PBase = kR32LdsBytes;
+constexpr int kR32Votes = kR32PBase;             // (after the step loop) 4 votes
+constexpr int kR32InvL = kR32PBase + 64;         // (after the step loop) 128 per-row 1/l
 constexpr int kR32PvLead = 4;                    // value MFMAs of step i before the scores of step i+1
-constexpr int kR32Ring = 4;                      // value operand reads in flight (one MFMA each)
 constexpr int kR32QkRing = 4;                    // score operand reads in flight
-constexpr int kR32LdsTotal = kR32LdsBytes + 512 + 16;
+constexpr int kR32LdsTotal = kR32PBase + 2 * kR32PBytes;
 static_assert(kR32LdsTotal <= 160 * 1024, "LDS budget");
 constexpr float kWindow = 64.f;                  // rows may exceed their reference max by 2^64
 static_assert(kDmaInstr % 4 == 0, "DMA split");
-static_assert(kR32PvLead % kR32Ring == 0 && kR32Ring <= kR32PvLead, "value operand ring turnover");
 static_assert(32 - kR32PvLead >= 23, "softmax pieces fit between the value MFMAs");
 
 // 16-B chunk swizzle within 8-chunk groups: physical = logical ^ sw(token). Over 16
@@ -188,8 +198,9 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   k_last = k_last < n_items - 1 ? k_last : n_items - 1;
   if (kb >= n_items || k_last < kb) return;
   const int rows_total = a.s_q * a.heads;
-  const QkAddr qk0 = qk_addr(0, lane);   // operand addresses in slot 0
-  const PvAddr pv0 = pv_addr(0, lane);
+  const QkAddr qk0 = qk_addr(0, lane);                        // operand addresses in slot 0
+  const PvAddr pv0 = pv_addr(256u * (uint32_t)wave, lane);    // (this wave's 128 channels)
+  const uint32_t plane = (uint32_t)kR32PBase + 16u * (uint32_t)lane;   // P tiles: 16 B per lane
 
   // Q^T B operand of item k: lane holds query row 32*wave + l%32 of the item's tile, channels
   // 16ks + 8(l/32) .. +7. Rows past the last query row (a partial tile) load the sequence's
@@ -392,6 +403,13 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       }
     };
     constexpr int kPieces = 23;
+    // this wave's P tiles (k-steps 0, 1) into P buffer b: tile (row block, k-step q) is 1 KiB
+    // at (2 row block + q) KiB, 16 B per lane, the A-operand layout
+    auto p_store = [&](int b, const bf16x8* pk) {
+      char __attribute__((address_space(3)))* dst = lds + (plane + b * kR32PBytes + wave * 2048);
+      *reinterpret_cast<bf16x8 __attribute__((address_space(3)))*>(dst) = pk[0];
+      *reinterpret_cast<bf16x8 __attribute__((address_space(3)))*>(dst + 1024) = pk[1];
+    };
 
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
@@ -399,12 +417,12 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
 #pragma unroll
       for (int c = 0; c < 16; ++c) o[c] = f32x16{};
       if (nsteps > 0) {
-      bf16x8 pcur[2];
-      bf16x8 pring[kR32Ring];   // value operand reads in flight
+      bf16x8 pcur[2];   // P of the current step for this wave's rows (A operands, k-steps 0, 1)
+      bf16x8 bq0[4];    // Z^T of the current step's k-step 0, this wave's channel tiles (B operands)
       uint32_t zc = (uint32_t)comp_slot * kBufBytes;
       wait_vmcnt<2 * kR32Dma>();   // data of step 0 (steps 1 and 2 may stay in flight)
       barrier_lds();
-      // scores and softmax of step 0
+      // scores and softmax of step 0; its P goes to P buffer 0
       {
         f32x16 s;
         bf16x8 qring[kR32QkRing];
@@ -420,12 +438,13 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         }
 #pragma unroll
         for (int p = 0; p < kPieces; ++p) softmax_piece(s, sg.hh0, true, p, pcur);
+        p_store(0, pcur);
         const PvAddr pa = pv_at(pv0, zc);
 #pragma unroll
-        for (int t = 0; t < kR32Ring; ++t) pring[t] = pv_read(pa, t);
+        for (int c = 0; c < 4; ++c) bq0[c] = pv_read(pa, c);
       }
       wait_vmcnt<kR32Dma>();      // data of step 1, for the first region's scores
-      barrier_lds();
+      barrier_lds();               // (and every wave's P of step 0)
 
       // Straight-line step body: the scores of step i+1 are computed also after the last
       // step (on whatever the next slot holds) and discarded, and a region past the end of
@@ -439,37 +458,37 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         const i32x4 rs = lc.k <= k_last ? cursor_rsrc<false>(lc, a, kv_ptr, nullptr).kv
                                         : make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
         const uint32_t lslot = lds_u32 + (uint32_t)load_slot * kBufBytes;
-        uint32_t voff = 0;        // source offset of the next DMA instruction (read 3 MFMAs ahead)
+        const uint32_t pbuf = plane + (uint32_t)(i & 1) * kR32PBytes;   // P of step i (this lane)
+        uint32_t voff = 0;        // source offset of the next DMA instruction (3 MFMAs ahead)
         f32x16 s;                 // scores of step i+1
-        bf16x8 pnext[2];          // P of step i+1
-        // value MFMA t of step i; the operand ring is refilled up to operand `limit`
-        auto pv_mfma = [&](const PvAddr& pa, int t, int limit) {
-          const bf16x8 cur = pring[t % kR32Ring];
-          if (t + kR32Ring < limit) pring[t % kR32Ring] = pv_read(pa, t + kR32Ring);
-          mfma_a(o[t & 15], pcur[t >> 4], cur);
+        bf16x8 pnext[2];          // P of step i+1, this wave's rows
+        // A operand of step i: P of row block (wave + g) % 4, k-step q (1 KiB per tile)
+        auto a_read = [&](int g, int q) -> bf16x8 {
+          const uint32_t rb = (uint32_t)((wave + g) & 3);
+          return lds_b128(lds + (pbuf + rb * 2048u + (uint32_t)q * 1024u));
         };
-        // 1) the first value MFMAs of step i (their first operands were read before the barrier)
-        {
-          const PvAddr pa = pv_at(pv0, zc);
+        // 1) the first value MFMAs of step i: this wave's rows, k-step 0, its four channel
+        //    tiles (operands in registers)
 #pragma unroll
-          for (int t = 0; t < kR32PvLead; ++t) {
-            pv_mfma(pa, t, kR32PvLead);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+        for (int c = 0; c < kR32PvLead; ++c) {
+          mfma_a(o[c], pcur[0], bq0[c]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // 2) scores of step i+1 with the DMA instructions of the step being loaded; the ring
-        //    turns over to the next value operands during the last score MFMAs
+        // 2) scores of step i+1 with the DMA instructions of the step being loaded; the P
+        //    tiles of the other row blocks (k-step 0) are read during the last score MFMAs
+        bf16x8 aq0[3];
         {
           bf16x8 qring[kR32QkRing];
           const QkAddr qa = qk_at(qk0, zn);
 #pragma unroll
           for (int t = 0; t < kR32QkRing; ++t) qring[t] = qk_read(qa, t);
-          const PvAddr pa = pv_at(pv0, zc);
 #pragma unroll
           for (int t = 0; t < 36; ++t) {
             const bf16x8 cur = qring[t % kR32QkRing];
             if (t + kR32QkRing < 36) qring[t % kR32QkRing] = qk_read(qa, t + kR32QkRing);
-            if (t + kR32Ring >= 36) pring[t % kR32Ring] = pv_read(pa, kR32PvLead + t + kR32Ring - 36);
+            if (t == 29) aq0[0] = a_read(1, 0);
+            if (t == 31) aq0[1] = a_read(2, 0);
+            if (t == 33) aq0[2] = a_read(3, 0);
             if (t == 0) mfma_v0(s, cur, qreg[0]);
             else mfma_v(s, cur, qreg[t]);
             if ((t & 3) == 0) voff = dma_voff(dmo, t >> 2);   // offset of the next DMA instruction
@@ -477,25 +496,43 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        // 3) the remaining value MFMAs of step i, the softmax of step i+1 between them
+        // 3) the remaining value MFMAs of step i, the softmax of step i+1 between them:
+        //    k-step 0 for the other row blocks, then k-step 1 channel tile by channel tile
         {
           const PvAddr pa = pv_at(pv0, zc);
+          bf16x8 bq1[3];   // ring of Z^T tiles of k-step 1
+          bf16x8 aq1[3];   // P tiles of k-step 1, the other row blocks
 #pragma unroll
           for (int t = kR32PvLead; t < 32; ++t) {
-            pv_mfma(pa, t, 32);
+            if (t == 6) bq1[0] = pv_read(pa, 16 + 0);
+            if (t == 8) aq1[0] = a_read(1, 1);
+            if (t == 9) aq1[1] = a_read(2, 1);
+            if (t == 10) aq1[2] = a_read(3, 1);
+            if (t == 12) bq1[1] = pv_read(pa, 16 + 1);
+            if (t == 16) bq1[2] = pv_read(pa, 16 + 2);
+            if (t == 20) bq1[0] = pv_read(pa, 16 + 3);
+            if (t < 16) {
+              const int g = 1 + (t - 4) / 4, c = (t - 4) % 4;
+              mfma_a(o[4 * g + c], aq0[g - 1], bq0[c]);
+            } else {
+              const int c = (t - 16) / 4, g = (t - 16) % 4;
+              mfma_a(o[4 * g + c], g == 0 ? pcur[1] : aq1[g == 0 ? 0 : g - 1], bq1[c % 3]);
+            }
             // one softmax piece after each value MFMA
             const int u = t - kR32PvLead;
             if (u < kPieces) softmax_piece(s, sg.hh0 + i + 1, live, u, pnext);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        // P of step i+1 for this wave's rows to the other P buffer (published by the barrier)
+        p_store((i + 1) & 1, pnext);
         pcur[0] = pnext[0];
         pcur[1] = pnext[1];
         // the first value operands of step i+1 (its rows were published at the last barrier)
         {
           const PvAddr pa = pv_at(pv0, zn);
 #pragma unroll
-          for (int t = 0; t < kR32Ring; ++t) pring[t] = pv_read(pa, t);
+          for (int c = 0; c < 4; ++c) bq0[c] = pv_read(pa, c);
         }
         // move the load cursor here: its scalar loads share the LDS counter, and the barrier
         // waits for that counter anyway
@@ -509,7 +546,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       // Did any row of the work-group leave the reference window? (vote through LDS)
       {
         int32_t __attribute__((address_space(3)))* vote =
-            (int32_t __attribute__((address_space(3)))*)(lds + kR32LdsBytes + 512);
+            (int32_t __attribute__((address_space(3)))*)(lds + kR32Votes);
         // (a NaN sum counts as out of range)
         const bool lane_bad = track ? window_exceeded : !(l_run <= 0x1p60f);
         const bool wave_exceeded = __ballot(lane_bad) != 0;   // (all lanes take part)
@@ -545,10 +582,11 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       for (int j = 0; j < kR32Slots - 1; ++j) issue_step();
     }
 
-    // ---- finalize (wave-local): out = O / l and lse = m + log2(l), or, for items the plan
-    // split, the unnormalised bf16 partial in register order plus (m, l). O tile c holds, in lane l
-    // and register r, row 8(r/4) + 4(l/32) + r%4 of the wave's 32 rows and channel
-    // 32c + l%32; the per-row 1/l comes from the row's lane through LDS.
+    // ---- finalize: out = O / l and lse = m + log2(l), or, for items the plan split, the
+    // unnormalised bf16 partial in register order plus (m, l). O tile 4g + c holds, in lane l
+    // and register r, row 8(r/4) + 4(l/32) + r%4 of row block (wave + g) % 4 and channel
+    // 128 wave + 32c + l%32; a row's 1/l, m and lse come from the wave that owns its softmax
+    // (rows 32 wave ..), its 1/l through LDS.
     {
       int l = lane;
       asm volatile("" : "+v"(l));
@@ -556,43 +594,55 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       const int f_seq = itf[kISeq], f_tile = itf[kITile];
       const bool split = itf[kINsplits] > 1;
       const int slot = split ? itf[kISlot] + (worker - itf[kIOwner]) : 0;
-      const int row0 = kRowsPerTile * f_tile + 32 * wave;   // the wave's first row in the item
-      float __attribute__((address_space(3)))* inv_s =
-          (float __attribute__((address_space(3)))*)(lds + kR32LdsBytes) + 32 * wave;
-      if (l < 32) inv_s[l] = l_run > 0.f ? 1.f / l_run : 0.f;
-      f32x4 inv4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) inv4[j] = *(const f32x4 __attribute__((address_space(3)))*)(inv_s + 8 * j + 4 * (l >> 5));
+      const int row0 = kRowsPerTile * f_tile + 32 * wave;   // the first row this wave owns
+      float __attribute__((address_space(3)))* inv_s = (float __attribute__((address_space(3)))*)(lds + kR32InvL);
+      if (!split) {
+        if (l < 32) inv_s[32 * wave + l] = l_run > 0.f ? 1.f / l_run : 0.f;
+        barrier_lds();   // every row's 1/l from the wave that owns it
+      }
       mfma_results_settle();
       if (split) {
         char* part = reinterpret_cast<char*>(ws) + (int64_t)slot * kSlotBytes;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          bf16x8 v0, v1;
+        for (int g = 0; g < 4; ++g) {
+          const int rb = (wave + g) & 3;
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {   // unnormalised: the combine divides by the denominator
-            v0[r] = (__bf16)o[c][r];
-            v1[r] = (__bf16)o[c][8 + r];
+          for (int c = 0; c < 4; ++c) {
+            bf16x8 v0, v1;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {   // unnormalised: the combine divides by the denominator
+              v0[r] = (__bf16)o[4 * g + c][r];
+              v1[r] = (__bf16)o[4 * g + c][8 + r];
+            }
+            // fragment (row block, channel tile 4 wave + c, lane)
+            char* dst = part + 32 * (int64_t)((rb * 16 + 4 * wave + c) * 64 + l);
+            *reinterpret_cast<bf16x8*>(dst) = v0;
+            *reinterpret_cast<bf16x8*>(dst + 16) = v1;
+            __builtin_amdgcn_sched_barrier(0);
           }
-          char* dst = part + 32 * (int64_t)((wave * 16 + c) * 64 + l);
-          *reinterpret_cast<bf16x8*>(dst) = v0;
-          *reinterpret_cast<bf16x8*>(dst + 16) = v1;
-          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int grow = row0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-          const bool ok = grow < rows_total;
-          const int jt = ok ? grow / a.heads : 0, hd = ok ? grow - jt * a.heads : 0;
-          float* dst = out_ptr + ((int64_t)(f_seq * a.s_q + jt) * a.heads + hd) * kLat + (l & 31);
-          const float sc = inv4[r >> 2][r & 3];
+        for (int g = 0; g < 4; ++g) {
+          const int rb = (wave + g) & 3;
+          f32x4 inv4[4];
 #pragma unroll
-          for (int c = 0; c < 16; ++c) {
-            const float v = o[c][r] * sc;
-            if (ok) dst[32 * c] = v;
+          for (int j = 0; j < 4; ++j)
+            inv4[j] = *(const f32x4 __attribute__((address_space(3)))*)(inv_s + 32 * rb + 8 * j + 4 * (l >> 5));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int grow = kRowsPerTile * f_tile + 32 * rb + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+            const bool ok = grow < rows_total;
+            const int jt = ok ? grow / a.heads : 0, hd = ok ? grow - jt * a.heads : 0;
+            float* dst = out_ptr + ((int64_t)(f_seq * a.s_q + jt) * a.heads + hd) * kLat + 128 * wave + (l & 31);
+            const float sc = inv4[r >> 2][r & 3];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float v = o[4 * g + c][r] * sc;
+              if (ok) dst[32 * c] = v;
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
       const int grow = row0 + (l & 31);
