@@ -77,6 +77,51 @@ def traffic_from_profile(kernel_srcs, key):
     return rec.get(key, {}).get("bytes_per_call")
 
 
+def projections(w, steps: int, warmup: int, copies: int = 16):
+    """The two projections around the attention at this workload's shape (tokens = b*s, h
+    heads), each timed with HIP events over `steps` calls on the launch stream, cycling
+    through `copies` sets of weights (more than the 256 MB Infinity Cache holds) with
+    seeded random values: query absorption (mla_absorb_query) and output decompression
+    (mla_decompress_output). Bytes are the algorithmic reads and writes of one call."""
+    import numpy as np
+    import torch
+    import mla_latent_space_amd as mla
+    dev = "cuda"
+    T, H = w.batch * w.s_q, w.heads
+    gen = torch.Generator(device=dev).manual_seed(5)
+    bf = lambda *shape: torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    q_nope, q_rope = bf(T, H, 128), bf(T, H, 64)
+    w_k = [bf(H, 512, 128) for _ in range(copies)]
+    w_v = [bf(H, 128, 512) for _ in range(copies)]
+    o_lat = torch.randn((T, H, 512), generator=gen, device=dev)
+    qz = torch.empty((T, H, 576), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H, 128), dtype=torch.float32, device=dev)
+    calls = {
+        "absorb_query": (lambda i: mla.absorb_query(q_nope, q_rope, w_k[i % copies], out=qz),
+                         T * H * (128 + 64 + 576) * 2 + H * 512 * 128 * 2),
+        "decompress_output": (lambda i: mla.decompress_output(o_lat, w_v[i % copies], out=out),
+                              T * H * (512 + 128) * 4 + H * 128 * 512 * 2),
+    }
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, (fn, byts) in calls.items():
+        for i in range(warmup):
+            fn(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        gbps = byts / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "bytes": byts, "flops": 2 * T * H * 512 * 128,
+                     "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                  "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
+    return res
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle (as is) over the workload's sequences, one at a time, until ~budget_s of
     host time (whole passes over the batch are repeated if one pass is shorter), scaled to
@@ -115,6 +160,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="KV copies to cycle through (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-projections", action="store_true",
+                    help="skip timing the query-absorption and output-decompression kernels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times (the reference "
                          "kernel for scaling HBM byte counters), print its size and exit")
@@ -236,6 +283,8 @@ def main():
         "roofline": dict(roof, kernel="mla_decode_fwd: decode kernel + split combine",
                          bytes_per_call=byts, flops_per_call=flops),
     }
+    if w.kv_dtype == "bf16" and not args.no_projections:
+        rec["projections"] = projections(w, args.steps, min(args.warmup, 50))
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -145,6 +145,40 @@ int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scal
                        float softmax_scale, int32_t causal, const void* plan, int32_t num_workers,
                        void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream);
 
+/* Query absorption (page "Mla Analysis", section "Absorption Trick (FlashMLA)": scoring the
+ * absorbed query against a latent row equals scoring the query against the decompressed
+ * key). Per token t and head h:
+ *   qz[t, h, 0:512]   = q_nope[t, h, :] . W_k[h]^T   (fp32 accumulation, rounded to bf16)
+ *   qz[t, h, 512:576] = q_rope[t, h, :]              (copied bit for bit)
+ * The result is the `q` argument of mla_decode_fwd.
+ *
+ * q_nope  device bf16 [tokens, heads, 128] (tokens = batch * s_q, row-major).
+ * q_rope  device bf16 [tokens, heads, 64] (rope rotation already applied).
+ * w_k     device bf16 [heads, 512, 128]: for each head and latent channel its 128
+ *         coefficients (the contraction index innermost).
+ * qz      device bf16 [tokens, heads, 576].
+ * All four 16-byte aligned and contiguous; tokens 1 .. 2,096,000, heads 1 .. 65535.
+ * Stream-ordered; allocates nothing. Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
+ * MLA_ERR_HIP. */
+int32_t mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int32_t tokens,
+                         int32_t heads, void* qz, void* stream);
+
+/* Output decompression (same page and section: softmax(A) (Z W_v) = (softmax(A) Z) W_v, so
+ * the value projection is applied once to the latent output, by a separate kernel after
+ * the attention). Per token t and head h:
+ *   out[t, h, :] = out_latent[t, h, :] . W_v[h]^T
+ * with out_latent rounded to bf16 on load and fp32 accumulation.
+ *
+ * out_latent  device float32 [tokens, heads, 512] (the `out` of mla_decode_fwd).
+ * w_v         device bf16 [heads, 128, 512]: for each head and output channel its 512
+ *             coefficients (the contraction index innermost; a linear layer's weight).
+ * out         device float32 [tokens, heads, 128].
+ * All three 16-byte aligned and contiguous; tokens 1 .. 2,096,000, heads 1 .. 65535.
+ * Stream-ordered; allocates nothing. Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
+ * MLA_ERR_HIP. */
+int32_t mla_decompress_output(const float* out_latent, const void* w_v, int32_t tokens, int32_t heads,
+                              float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["MlaError", "SplitPlan", "lib", "abi_version", "default_num_workers", "plan_bytes", "workspace_bytes",
+           "absorb_query", "decompress_output",
            "get_split_plan", "decode_fwd", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -61,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_fwd.restype = c_i32
     L.mla_decode_fwd.argtypes = [c_p, c_p, c_p, c_i32, c_i64, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_f, c_i32,
                                  c_p, c_i32, c_p, c_sz, c_p, c_p, c_p]
+    L.mla_absorb_query.restype = c_i32
+    L.mla_absorb_query.argtypes = [c_p, c_p, c_p, c_i32, c_i32, c_p, c_p]
+    L.mla_decompress_output.restype = c_i32
+    L.mla_decompress_output.argtypes = [c_p, c_p, c_i32, c_i32, c_p, c_p]
     _lib = L
     return L
 
@@ -171,3 +176,47 @@ def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         out.data_ptr(), lse.data_ptr(), _stream(q))
     _check(int(status))
     return out, lse
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape):
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous CUDA {dtype} tensor of shape {tuple(shape)}")
+
+
+def absorb_query(q_nope: torch.Tensor, q_rope: torch.Tensor, w_k: torch.Tensor,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Qz = [q_nope W_k^T | q_rope] per head (see mla_absorb_query). q_nope bf16 [..., h, 128],
+    q_rope bf16 [..., h, 64], w_k bf16 [h, 512, 128]; returns bf16 [..., h, 576]."""
+    lead = tuple(q_nope.shape[:-2])
+    heads = q_nope.shape[-2]
+    tokens = 1
+    for x in lead:
+        tokens *= int(x)
+    _need(q_nope, "q_nope", torch.bfloat16, lead + (heads, 128))
+    _need(q_rope, "q_rope", torch.bfloat16, lead + (heads, 64))
+    _need(w_k, "w_k", torch.bfloat16, (heads, 512, 128))
+    if out is None:
+        out = torch.empty(lead + (heads, 576), dtype=torch.bfloat16, device=q_nope.device)
+    _need(out, "out", torch.bfloat16, lead + (heads, 576))
+    _check(int(lib().mla_absorb_query(q_nope.data_ptr(), q_rope.data_ptr(), w_k.data_ptr(), tokens, heads,
+                                      out.data_ptr(), _stream(q_nope))))
+    return out
+
+
+def decompress_output(out_latent: torch.Tensor, w_v: torch.Tensor,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = O_latent W_v^T per head (see mla_decompress_output). out_latent float32
+    [..., h, 512], w_v bf16 [h, 128, 512]; returns float32 [..., h, 128]."""
+    lead = tuple(out_latent.shape[:-2])
+    heads = out_latent.shape[-2]
+    tokens = 1
+    for x in lead:
+        tokens *= int(x)
+    _need(out_latent, "out_latent", torch.float32, lead + (heads, 512))
+    _need(w_v, "w_v", torch.bfloat16, (heads, 128, 512))
+    if out is None:
+        out = torch.empty(lead + (heads, 128), dtype=torch.float32, device=out_latent.device)
+    _need(out, "out", torch.float32, lead + (heads, 128))
+    _check(int(lib().mla_decompress_output(out_latent.data_ptr(), w_v.data_ptr(), tokens, heads, out.data_ptr(),
+                                           _stream(out_latent))))
+    return out

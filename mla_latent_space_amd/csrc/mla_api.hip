@@ -176,4 +176,34 @@ int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scal
   return ok();
 }
 
+int32_t mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int32_t tokens, int32_t heads,
+                         void* qz, void* stream) {
+  if (!q_nope || !q_rope || !w_k || !qz)
+    return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL (q_nope, q_rope, w_k, qz)");
+  if (tokens < 1) return fail(MLA_ERR_INVALID_ARG, "tokens must be >= 1 (got %d)", tokens);
+  if (heads < 1) return fail(MLA_ERR_INVALID_ARG, "heads must be >= 1 (got %d)", heads);
+  if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "heads must be <= 65535 (got %d)", heads);
+  if ((int64_t)tokens > 32LL * 65535) return fail(MLA_ERR_UNSUPPORTED, "tokens must be <= %d", 32 * 65535);
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_k) || !aligned16(qz))
+    return fail(MLA_ERR_INVALID_ARG, "q_nope, q_rope, w_k and qz must be 16-byte aligned");
+  hipError_t e = mla::launch_absorb_query(q_nope, q_rope, w_k, tokens, heads, qz, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "absorption kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t mla_decompress_output(const float* out_latent, const void* w_v, int32_t tokens, int32_t heads, float* out,
+                              void* stream) {
+  if (!out_latent || !w_v || !out)
+    return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL (out_latent, w_v, out)");
+  if (tokens < 1) return fail(MLA_ERR_INVALID_ARG, "tokens must be >= 1 (got %d)", tokens);
+  if (heads < 1) return fail(MLA_ERR_INVALID_ARG, "heads must be >= 1 (got %d)", heads);
+  if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "heads must be <= 65535 (got %d)", heads);
+  if ((int64_t)tokens > 32LL * 65535) return fail(MLA_ERR_UNSUPPORTED, "tokens must be <= %d", 32 * 65535);
+  if (!aligned16(out_latent) || !aligned16(w_v) || !aligned16(out))
+    return fail(MLA_ERR_INVALID_ARG, "out_latent, w_v and out must be 16-byte aligned");
+  hipError_t e = mla::launch_decompress_output(out_latent, w_v, tokens, heads, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decompression kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

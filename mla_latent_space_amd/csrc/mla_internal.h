@@ -9,6 +9,8 @@ constexpr int kPage = 64;          // tokens per cache page
 constexpr int kLat = 512;          // latent (c_KV) channels, the value width
 constexpr int kRope = 64;          // shared rope key channels
 constexpr int kDqk = kLat + kRope; // 576: absorbed query / cached row width
+constexpr int kNope = 128;         // per-head query channels before absorption
+constexpr int kDv = 128;           // per-head value channels after decompression
 constexpr int kRowsPerTile = 128;  // query rows (token, head) per work item
 constexpr int kFp8RowBytes = kLat + 2 * kRope;  // 640
 constexpr int kFp8Tiles = kLat / 128;           // 4 scales per token
@@ -79,5 +81,9 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_rows32(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int tokens, int heads,
+                               void* qz, hipStream_t stream);
+hipError_t launch_decompress_output(const float* out_latent, const void* w_v, int tokens, int heads, float* out,
+                                    hipStream_t stream);
 
 }  // namespace mla

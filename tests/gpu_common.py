@@ -10,9 +10,11 @@ import mla_latent_space_amd as mla
 # <= 2e-2, |d lse| <= 1e-3. fp8 cache: compared with the oracle on the same dequantised
 # values, rel L2 <= 3e-2 (the stated fp8 bound). Its max abs and lse bounds follow from
 # the arithmetic: the kernel dequantises each value once into bf16 (relative error
-# <= 2^-9), which moves a score by at most softmax_scale * 2^-9 * sum_c |q_c z_c| (about
-# 5e-2 worst case and 3e-3 typical for these N(0,1) draws); lse moves by no more than the
-# largest score error, so fp8 lse is held to 2e-2 and max abs keeps the bf16 bound.
+# <= 2^-8, the unit roundoff of an 8-bit significand), which moves a score by at most
+# softmax_scale * 2^-8 * sum_c |q_c z_c| (about 1e-1 in the worst case and 6e-3 typical for
+# these N(0,1) draws, whose per-value errors have random signs); lse moves by no more than
+# the largest score error, so fp8 lse is held to 2e-2, about three times the typical
+# perturbation, and max abs keeps the bf16 bound.
 BF16_TOL = dict(rel_l2=5e-3, max_abs=2e-2, lse=1e-3)
 FP8_TOL = dict(rel_l2=3e-2, max_abs=2e-2, lse=2e-2)
 

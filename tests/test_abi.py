@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"mla_get_split_plan", "mla_decode_fwd", "mla_plan_bytes", "mla_workspace_bytes"} <= set(names)
+    assert {"mla_get_split_plan", "mla_decode_fwd", "mla_plan_bytes", "mla_workspace_bytes", "mla_absorb_query",
+            "mla_decompress_output"} <= set(names)
     L = ctypes.CDLL(mla.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -96,4 +97,19 @@ def test_decode_rejects_bad_arguments_before_launch():
     assert _decode(L, ws_bytes=16) == 3
     assert _decode(L, ws=None) == 3
     assert _decode(L, out=ctypes.c_void_p(0x100008)) == 1  # misaligned
+    assert b"16-byte aligned" in L.mla_last_error_message()
+
+
+def test_projections_reject_bad_arguments_before_launch():
+    """Null pointers, empty shapes and misaligned buffers return a status before anything is
+    enqueued (fake, never dereferenced device addresses; no GPU needed)."""
+    L = mla.lib()
+    fake = 1 << 20
+    assert L.mla_absorb_query(None, fake, fake, 4, 16, fake, None) == 1
+    assert L.mla_absorb_query(fake, fake, fake, 0, 16, fake, None) == 1
+    assert L.mla_absorb_query(fake, fake, fake, 4, 0, fake, None) == 1
+    assert L.mla_absorb_query(fake + 8, fake, fake, 4, 16, fake, None) == 1
+    assert L.mla_decompress_output(fake, None, 4, 16, fake, None) == 1
+    assert L.mla_decompress_output(fake, fake, -1, 16, fake, None) == 1
+    assert L.mla_decompress_output(fake, fake, 4, 16, fake + 4, None) == 1
     assert b"16-byte aligned" in L.mla_last_error_message()
