@@ -157,7 +157,8 @@ int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scal
  * w_k     device bf16 [heads, 512, 128]: for each head and latent channel its 128
  *         coefficients (the contraction index innermost).
  * qz      device bf16 [tokens, heads, 576].
- * All four 16-byte aligned and contiguous; tokens 1 .. 2,096,000, heads 1 .. 65535.
+ * All four 16-byte aligned and contiguous; tokens 1 .. 2,097,120, heads 1 .. 65535,
+ * tokens * heads < 2^24.
  * Stream-ordered; allocates nothing. Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
  * MLA_ERR_HIP. */
 int32_t mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int32_t tokens,
@@ -173,7 +174,8 @@ int32_t mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_k
  * w_v         device bf16 [heads, 128, 512]: for each head and output channel its 512
  *             coefficients (the contraction index innermost; a linear layer's weight).
  * out         device float32 [tokens, heads, 128].
- * All three 16-byte aligned and contiguous; tokens 1 .. 2,096,000, heads 1 .. 65535.
+ * All three 16-byte aligned and contiguous; tokens 1 .. 2,097,120, heads 1 .. 65535,
+ * tokens * heads < 2^21.
  * Stream-ordered; allocates nothing. Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
  * MLA_ERR_HIP. */
 int32_t mla_decompress_output(const float* out_latent, const void* w_v, int32_t tokens, int32_t heads,

@@ -184,6 +184,8 @@ int32_t mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_k
   if (heads < 1) return fail(MLA_ERR_INVALID_ARG, "heads must be >= 1 (got %d)", heads);
   if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "heads must be <= 65535 (got %d)", heads);
   if ((int64_t)tokens > 32LL * 65535) return fail(MLA_ERR_UNSUPPORTED, "tokens must be <= %d", 32 * 65535);
+  if ((int64_t)tokens * heads * mla::kNope * 2 > 0xFFFFFFFFLL)
+    return fail(MLA_ERR_UNSUPPORTED, "tokens * heads must be below 2^24 (got %lld)", (long long)tokens * heads);
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_k) || !aligned16(qz))
     return fail(MLA_ERR_INVALID_ARG, "q_nope, q_rope, w_k and qz must be 16-byte aligned");
   hipError_t e = mla::launch_absorb_query(q_nope, q_rope, w_k, tokens, heads, qz, static_cast<hipStream_t>(stream));
@@ -199,6 +201,8 @@ int32_t mla_decompress_output(const float* out_latent, const void* w_v, int32_t 
   if (heads < 1) return fail(MLA_ERR_INVALID_ARG, "heads must be >= 1 (got %d)", heads);
   if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "heads must be <= 65535 (got %d)", heads);
   if ((int64_t)tokens > 32LL * 65535) return fail(MLA_ERR_UNSUPPORTED, "tokens must be <= %d", 32 * 65535);
+  if ((int64_t)tokens * heads * mla::kLat * 4 > 0xFFFFFFFFLL)
+    return fail(MLA_ERR_UNSUPPORTED, "tokens * heads must be below 2^21 (got %lld)", (long long)tokens * heads);
   if (!aligned16(out_latent) || !aligned16(w_v) || !aligned16(out))
     return fail(MLA_ERR_INVALID_ARG, "out_latent, w_v and out must be 16-byte aligned");
   hipError_t e = mla::launch_decompress_output(out_latent, w_v, tokens, heads, out, static_cast<hipStream_t>(stream));

@@ -6,45 +6,37 @@
 //  * output decompression: out[t, h] = O_latent[t, h] W_v[h]^T, W_v[h] of shape [128, 512]
 //    (one row of 512 coefficients per output channel, the usual linear-layer layout); the
 //    page leaves this to a separate kernel after the attention.
-// In both, the contraction index is the innermost one of both operands, so an MFMA operand
-// fragment (8 consecutive k of one row) is one 16-byte load and no staging is needed. One
-// work-group per (128 output columns, 32 rows, head); wave w takes columns 32w .. 32w+31,
-// the k loop runs in chunks of 8 MFMAs with all their operand loads in flight. The decode's
-// fp32 O_latent is rounded to bf16 on load.
-#include "mla_internal.h"
+// In both, the contraction index is the innermost one of both operands. One work-group per
+// (128 output columns, 32 rows, head); wave w takes columns 32w .. 32w+31. The k loop runs in
+// chunks of 128: the chunk's operand blocks are copied into LDS by LDS-DMA (1 KiB contiguous
+// per instruction; loaded straight into MFMA fragments, every load instruction would touch
+// 32 rows), 16-byte chunks XOR-swizzled by row so that the fragment reads (32 rows x one
+// chunk) are free of bank conflicts, then 8 MFMAs per wave. Rows past the last token read as
+// zeros (buffer range check). The decode's fp32 O_latent is rounded to bf16 when read.
+#include "mla_device.h"
 
 namespace mla {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 pbf16x8;
-typedef __attribute__((ext_vector_type(4))) float pf32x4;
-typedef __attribute__((ext_vector_type(16))) float pf32x16;
-
 constexpr int kProjThreads = 256;
-constexpr int kProjChunk = 8;   // k-steps (16 each) per chunk
+constexpr int kProjKc = 128;                  // k per chunk
+constexpr int kProjBBytes = 128 * kProjKc * 2;   // B block: 128 rows x 128 k, bf16 (32 KiB)
 
-template <bool kAFloat>
-__device__ __forceinline__ pbf16x8 load_a(const void* a, int64_t idx, bool ok) {
-  pbf16x8 v;
-  if (kAFloat) {
-    const float* p = static_cast<const float*>(a) + idx;
-    const pf32x4 lo = ok ? *reinterpret_cast<const pf32x4*>(p) : pf32x4{0.f, 0.f, 0.f, 0.f};
-    const pf32x4 hi = ok ? *reinterpret_cast<const pf32x4*>(p + 4) : pf32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = (__bf16)lo[i];
-      v[4 + i] = (__bf16)hi[i];
-    }
-  } else {
-    const __bf16* p = static_cast<const __bf16*>(a) + idx;
-    if (ok) {
-      v = *reinterpret_cast<const pbf16x8*>(p);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.f;
-    }
+// LDS-DMA of a block of `rows` rows x kProjKc elements of `esz` bytes from a row-major source
+// (row stride `src_stride` bytes, block start at byte `src0` of the buffer): LDS holds row r at
+// r * row_bytes with chunk c' holding source chunk c' ^ (r % 16). The work-group's 256
+// threads issue the 1-KiB instructions in turn.
+__device__ __forceinline__ void stage_block(const i32x4& rsrc, uint32_t lds_dst, uint32_t src0, uint32_t src_stride,
+                                            int rows, int esz, int tid) {
+  const int row_chunks = kProjKc * esz / 16;           // 16 (bf16) or 32 (fp32)
+  const int instrs = rows * row_chunks / 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int i = wave; i < instrs; i += 4) {
+    const int p = 64 * i + lane;
+    const int r = p / row_chunks, cp = p % row_chunks;
+    const int c = cp ^ (r & 15);
+    lds_dma_x4(lds_dst + 1024u * (uint32_t)i, src0 + (uint32_t)r * src_stride + 16u * (uint32_t)c, rsrc);
   }
-  return v;
 }
 
 // C[t, h, n] = sum_k A[t, h, k] B[h, n, k] for n < N (A rows of K elements, C rows of ldc
@@ -53,56 +45,81 @@ template <bool kAFloat, bool kCBf16>
 __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restrict__ A, const __bf16* __restrict__ B,
                                                             void* __restrict__ C, const __bf16* __restrict__ rope,
                                                             int T, int H, int K, int N, int ldc) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.z, m0 = 32 * blockIdx.y, n0 = 128 * blockIdx.x + 32 * wave;
-  const int row = m0 + (lane & 31);
-  const bool row_ok = row < T;
-  const int kh = 8 * (lane >> 5);
-  const int64_t a_row = ((int64_t)(row_ok ? row : 0) * H + h) * K + kh;
-  const bool col_ok = n0 < N;   // (N is a multiple of 32)
-  const int64_t b_row = ((int64_t)h * N + (col_ok ? n0 : 0) + (lane & 31)) * K + kh;
-  pf32x16 acc;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  char __attribute__((address_space(3)))* lds = (char __attribute__((address_space(3)))*)smem_raw;
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
+  constexpr int esz = kAFloat ? 4 : 2;
+  constexpr int a_row_bytes = kProjKc * esz;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.z, m0 = 32 * blockIdx.y, nb = 128 * blockIdx.x;
+  // A: all T rows of head h; row m at byte (m H + h) K esz; the range check zero-fills m >= T
+  const i32x4 ra = make_rsrc(reinterpret_cast<uint64_t>(A), (int)((int64_t)T * H * K * esz));
+  // B: rows nb .. nb+127 of head h, K elements each
+  const i32x4 rb = make_rsrc(reinterpret_cast<uint64_t>(B) + ((uint64_t)h * N + nb) * K * 2, 128 * K * 2);
+  const uint32_t a_lds = lds_u32 + kProjBBytes;
+  f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  for (int kc = 0; kc < K; kc += 16 * kProjChunk) {
-    pbf16x8 af[kProjChunk], bfr[kProjChunk];
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int nrow = 32 * wave + l32;   // this lane's row of the B block
+  for (int kc = 0; kc < K; kc += kProjKc) {
+    stage_block(rb, lds_u32, (uint32_t)kc * 2, (uint32_t)K * 2, 128, 2, tid);
+    stage_block(ra, a_lds, (uint32_t)(((int64_t)m0 * H + h) * K + kc) * esz, (uint32_t)H * K * esz, 32, esz, tid);
+    wait_vmcnt<0>();
+    barrier_lds();
 #pragma unroll
-    for (int j = 0; j < kProjChunk; ++j) {
-      af[j] = load_a<kAFloat>(A, a_row + kc + 16 * j, row_ok);
-      bfr[j] = *reinterpret_cast<const pbf16x8*>(B + b_row + kc + 16 * j);
+    for (int j = 0; j < kProjKc / 16; ++j) {
+      const int c = 2 * j + hh;   // logical 16-B chunk of k 16j + 8hh .. +7 (bf16)
+      const bf16x8 bf = lds_b128(lds + (nrow * 256 + 16 * (c ^ (nrow & 15))));
+      bf16x8 af;
+      if (kAFloat) {
+        // fp32: the 8 values are logical chunks 2c, 2c+1 of a 512-B row
+        const f32x4 lo = *(const f32x4 __attribute__((address_space(3)))*)(lds + (kProjBBytes + l32 * a_row_bytes +
+                                                                                    16 * ((2 * c) ^ (l32 & 15))));
+        const f32x4 hi = *(const f32x4 __attribute__((address_space(3)))*)(lds + (kProjBBytes + l32 * a_row_bytes +
+                                                                                    16 * ((2 * c + 1) ^ (l32 & 15))));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          af[i] = (__bf16)lo[i];
+          af[4 + i] = (__bf16)hi[i];
+        }
+      } else {
+        af = lds_b128(lds + (kProjBBytes + l32 * a_row_bytes + 16 * (c ^ (l32 & 15))));
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < kProjChunk; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j], bfr[j], acc, 0, 0, 0);
+    barrier_lds();   // the blocks are read before the next chunk overwrites them
   }
-  if (col_ok) {
-    // acc register r of lane l: row m0 + 8(r/4) + 4(l/32) + r%4, column n0 + l%32
+  const int n0 = nb + 32 * wave;
+  // acc register r of lane l: row m0 + 8(r/4) + 4(l/32) + r%4, column n0 + l%32
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (m >= T) continue;
-      const int64_t ci = ((int64_t)m * H + h) * ldc + n0 + (lane & 31);
-      if (kCBf16) static_cast<__bf16*>(C)[ci] = (__bf16)acc[r];
-      else static_cast<float*>(C)[ci] = acc[r];
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+    if (m >= T) continue;
+    const int64_t ci = ((int64_t)m * H + h) * ldc + n0 + l32;
+    if (kCBf16) static_cast<__bf16*>(C)[ci] = (__bf16)acc[r];
+    else static_cast<float*>(C)[ci] = acc[r];
   }
   if (rope != nullptr && blockIdx.x == 0) {
     // 32 rows x 64 rope values (128 B per row): one 16-B chunk per thread
-    const int rr = threadIdx.x >> 3, ch = threadIdx.x & 7;
+    const int rr = tid >> 3, ch = tid & 7;
     const int m = m0 + rr;
     if (m < T) {
       const int64_t src = ((int64_t)m * H + h) * 64 + 8 * ch;
       const int64_t dst = ((int64_t)m * H + h) * ldc + N + 8 * ch;
-      *reinterpret_cast<pbf16x8*>(static_cast<__bf16*>(C) + dst) = *reinterpret_cast<const pbf16x8*>(rope + src);
+      *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(C) + dst) = *reinterpret_cast<const bf16x8*>(rope + src);
     }
   }
 }
+
+constexpr int proj_lds_bytes(bool a_float) { return kProjBBytes + 32 * kProjKc * (a_float ? 4 : 2); }
 
 }  // namespace
 
 hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int tokens, int heads,
                                void* qz, hipStream_t stream) {
   const dim3 grid(kLat / 128, (tokens + 31) / 32, heads);
-  hipLaunchKernelGGL((proj_kernel<false, true>), grid, dim3(kProjThreads), 0, stream, q_nope,
+  hipLaunchKernelGGL((proj_kernel<false, true>), grid, dim3(kProjThreads), proj_lds_bytes(false), stream, q_nope,
                      static_cast<const __bf16*>(w_k), qz, static_cast<const __bf16*>(q_rope), tokens, heads,
                      kNope, kLat, kDqk);
   return hipGetLastError();
@@ -111,7 +128,7 @@ hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const voi
 hipError_t launch_decompress_output(const float* out_latent, const void* w_v, int tokens, int heads, float* out,
                                     hipStream_t stream) {
   const dim3 grid(1, (tokens + 31) / 32, heads);
-  hipLaunchKernelGGL((proj_kernel<true, false>), grid, dim3(kProjThreads), 0, stream,
+  hipLaunchKernelGGL((proj_kernel<true, false>), grid, dim3(kProjThreads), proj_lds_bytes(true), stream,
                      static_cast<const void*>(out_latent), static_cast<const __bf16*>(w_v), static_cast<void*>(out),
                      static_cast<const __bf16*>(nullptr), tokens, heads, kLat, kDv, kDv);
   return hipGetLastError();
