@@ -165,13 +165,9 @@ int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scal
   a.out = out;
   a.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // bf16 cache: four-wave kernel (32 query rows per wave); fp8 cache: eight-wave kernel with
-  // a dequantising stage
-  const bool rows32 = kv_dtype == MLA_KV_BF16;
-  hipError_t e = rows32 ? mla::launch_decode_rows32(a, s) : mla::launch_decode_fp8(a, s);
-  if (e == hipErrorNotSupported) return fail(MLA_ERR_UNSUPPORTED, "this cache dtype is not built in this library");
+  hipError_t e = mla::launch_decode_rows32(a, kv_dtype == MLA_KV_FP8_E4M3, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
-  e = rows32 ? mla::launch_combine_rows32(a, s) : mla::launch_combine(a, s);
+  e = mla::launch_combine_rows32(a, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
   return ok();
 }

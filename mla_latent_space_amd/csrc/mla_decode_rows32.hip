@@ -50,12 +50,26 @@ constexpr int kR32Dma = kDmaInstr / 4;           // 9 LDS-DMA instructions per w
 constexpr int kR32LdsBytes = kR32Slots * kBufBytes;   // the ring; then two P buffers
 constexpr int kR32PBytes = kRowsPerTile * kStep * 2;  // P of one step: 128 rows x 32 tokens, bf16
 constexpr int kR32PBase = kR32LdsBytes;
-constexpr int kR32Votes = kR32PBase;             // (after the step loop) 4 votes
-constexpr int kR32InvL = kR32PBase + 64;         // (after the step loop) 128 per-row 1/l
 constexpr int kR32PvLead = 4;                    // value MFMAs of step i before the scores of step i+1
 constexpr int kR32QkRing = 4;                    // score operand reads in flight
+constexpr int kF8QkRing = 3;                     // (fp8 cache)
 constexpr int kR32LdsTotal = kR32PBase + 2 * kR32PBytes;
 static_assert(kR32LdsTotal <= 160 * 1024, "LDS budget");
+// fp8 cache: two slots of dequantised steps (bf16, the ring layout above), three staging
+// slots of raw steps as loaded, then the two P buffers.
+constexpr int kR8Bf16Slots = 2;
+constexpr int kR8Stage = 3;
+constexpr int kR8StRope = kStep * kLat;                      // codes: 32 rows of 512 B
+constexpr int kR8StScales = kR8StRope + kStep * 2 * kRope;   // rope: 32 rows of 128 B
+constexpr int kR8StBytes = kR8StScales + 1024;               // scales: 32 x 16 B (+ 512 B of zeros)
+constexpr int kR8StBase = kR8Bf16Slots * kBufBytes;
+constexpr int kR8PBase = kR8StBase + kR8Stage * kR8StBytes;
+constexpr int kR8QBase = kR8PBase + 2 * kR32PBytes;         // Q^T k-steps 34, 35 (2 KiB per wave)
+constexpr int kR8LdsTotal = kR8QBase + 4 * 2048;
+static_assert(kR8LdsTotal <= 160 * 1024, "LDS budget (fp8)");
+static_assert(kR8LdsTotal >= kR32Slots * kBufBytes, "the query rows are staged through LDS at start-up");
+static_assert(kR8StBase % 128 == 0 && kR8StBytes % 128 == 0 && kBufBytes % 128 == 0,
+              "slot offsets leave the low 7 address bits to the lane's swizzle");
 constexpr float kWindow = 64.f;                  // rows may exceed their reference max by 2^64
 static_assert(kDmaInstr % 4 == 0, "DMA split");
 static_assert(32 - kR32PvLead >= 23, "softmax pieces fit between the value MFMAs");
@@ -92,6 +106,45 @@ __device__ __forceinline__ uint32_t dma_voff(const DmaOffsets& d, int n) {
 }
 __device__ __forceinline__ void issue32(const i32x4& rsrc, uint32_t lds_slot, int n, uint32_t voff, int wave) {
   lds_dma_x4(lds_slot + 1024u * (uint32_t)(wave + 4 * n), voff, rsrc);
+}
+
+// fp8 staging slot of one step, filled by 21 LDS-DMA instructions:
+//  * codes: token u's 512 codes at 512u, its 32-B pieces (32 channels) permuted within each
+//    256-B half by piece ^ (u % 8), so that the dequantisation's reads of 8 tokens x one
+//    32-channel piece cover all 64 banks. Instruction n (1 KiB: tokens 2n, 2n+1) is issued
+//    by wave n % 4, so a lane's permutation is the same for all its instructions and
+//    instruction n = wave + 4m reads at base + 8 * 640 m.
+//  * rope: token u's 128 B at 16384 + 128u, one instruction per wave (8 tokens);
+//  * scales: 32 x 4 floats at 20480, one instruction by wave 0 (lanes 32.. read past the
+//    range and write zeros after them).
+// The (token, byte) -> (LDS position) map is a permutation of 16-B units, so every source
+// byte lands once.
+struct F8Dma { uint32_t codes, rope, scales; };
+__device__ __forceinline__ F8Dma f8_dma_offsets(int wave, int lane) {
+  const uint32_t l = (uint32_t)lane, u0 = 2u * (uint32_t)wave + (l >> 5);
+  F8Dma d;
+  d.codes = u0 * kF8Row + 16u * ((l & 31u) ^ (2u * (u0 & 7u)));
+  d.rope = (8u * (uint32_t)wave + (l >> 3)) * kF8Row + kLat + 16u * (l & 7u);
+  d.scales = l < 32u ? 16u * l : 0x40000000u;
+  return d;
+}
+// Four e4m3fn codes (one word, channel order) times their tile's scale: the fp32 product
+// rounded to bf16.
+__device__ __forceinline__ bf16x4 dequant4(uint32_t w, float sc) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  bf16x4 r;
+  r[0] = (__bf16)(lo[0] * sc);
+  r[1] = (__bf16)(lo[1] * sc);
+  r[2] = (__bf16)(hi[0] * sc);
+  r[3] = (__bf16)(hi[1] * sc);
+  return r;
+}
+// s_waitcnt for the fp8 DMA steps: wave 0 issues 6 instructions per step, the others 5
+template <int kSteps>
+__device__ __forceinline__ void wait_f8_steps(int wave) {
+  if (wave == 0) wait_vmcnt<6 * kSteps>();
+  else wait_vmcnt<5 * kSteps>();
 }
 
 // v_mfma_f32_32x32x16_bf16 with the accumulator in VGPRs (scores) or AGPRs (values). A VALU
@@ -178,10 +231,13 @@ __device__ __forceinline__ PvAddr pv_at(const PvAddr& base, uint32_t zoff) {
   return r;
 }
 
+template <bool kFp8>
 __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
-    const __bf16* __restrict__ q_ptr, const char* __restrict__ kv_ptr, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seqlens, const int32_t* __restrict__ plan, float* __restrict__ ws,
+    const __bf16* __restrict__ q_ptr, const char* __restrict__ kv_ptr, const float* __restrict__ kv_scales,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ plan, float* __restrict__ ws,
     float* __restrict__ out_ptr, float* __restrict__ lse_ptr, Scalars a) {
+  constexpr int kPBase = kFp8 ? kR8PBase : kR32PBase;   // P buffers; votes and 1/l after the loop
+  constexpr int kLoadSlots = kFp8 ? kR8Stage : kR32Slots;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   char __attribute__((address_space(3)))* lds = (char __attribute__((address_space(3)))*)smem_raw;
   const int lane = threadIdx.x & 63;
@@ -200,7 +256,12 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   const int rows_total = a.s_q * a.heads;
   const QkAddr qk0 = qk_addr(0, lane);                        // operand addresses in slot 0
   const PvAddr pv0 = pv_addr(256u * (uint32_t)wave, lane);    // (this wave's 128 channels)
-  const uint32_t plane = (uint32_t)kR32PBase + 16u * (uint32_t)lane;   // P tiles: 16 B per lane
+  const uint32_t plane = (uint32_t)kPBase + 16u * (uint32_t)lane;   // P tiles: 16 B per lane
+  // fp8: Q^T k-step ks (34, 35) of this lane in LDS
+  auto q_lds_addr = [&](int ks) -> uint32_t {
+    return (uint32_t)kR8QBase + 2048u * (uint32_t)wave + 1024u * (uint32_t)(ks - 34) + 16u * (uint32_t)lane;
+  };
+  auto q_lds = [&](int ks) -> bf16x8 { return lds_b128(lds + q_lds_addr(ks)); };
 
   // Q^T B operand of item k: lane holds query row 32*wave + l%32 of the item's tile, channels
   // 16ks + 8(l/32) .. +7. Rows past the last query row (a partial tile) load the sequence's
@@ -235,22 +296,119 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   };
   settle();
   if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
-  int load_slot = 0;
+  int load_slot = 0;   // ring slot (bf16) or staging slot (fp8) of the cursor's step
   auto advance = [&]() {
-    load_slot = load_slot + 1 == kR32Slots ? 0 : load_slot + 1;
+    load_slot = load_slot + 1 == kLoadSlots ? 0 : load_slot + 1;
     ++lc.hh;
     settle();
     if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
   };
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
   const DmaOffsets dmo = dma_offsets(wave, lane);   // this wave's DMA source offsets
-  // one step of the load cursor into the ring (zero-record loads past the worker's range)
+  // descriptors of the cursor's step (zero-record loads past the worker's range)
+  auto step_rsrc = [&]() -> StepRsrc {
+    if (lc.k <= k_last) return cursor_rsrc<kFp8>(lc, a, kv_ptr, kv_scales);
+    StepRsrc z;
+    z.kv = z.sc = make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
+    return z;
+  };
+  // fp8: this lane's DMA source offsets and its addresses for dequantising (token
+  // 16 half + l/4, channels 128 wave + 32c + 8(l%4) .. +7 of piece c: the staging read, where
+  // XOR 32c selects the piece; the bf16 slot write, where XOR 64 (c%2) plus 128 (c/2) does;
+  // the scale) and for copying the rope (token 8 wave + l/8, 16 B), packed two 16-bit
+  // offsets per register
+  uint32_t f8_dma = 0, f8_dq = 0, f8_aux = 0;
+  if constexpr (kFp8) {
+    const uint32_t l = (uint32_t)lane, u = l >> 2, sub = l & 3u, ur = 8u * (uint32_t)wave + (l >> 3);
+    const F8Dma d = f8_dma_offsets(wave, lane);
+    f8_dma = d.codes | (d.rope << 16);
+    f8_dq = (u * kLat + ((128u * (uint32_t)wave + 8u * sub) ^ (32u * (u & 7u)))) |
+            ((u * kRowBytes + 256u * (uint32_t)wave + 16u * (sub ^ sw32(u))) << 16);
+    f8_aux = (kR8StScales + 16u * u + 4u * (uint32_t)wave) | ((ur * kRowBytes + 16u * (64u + ((l & 7u) ^ sw32(ur)))) << 16);
+    static_assert(kR8StBytes < 65536 && 16 * kRowBytes < 65536 && kBufBytes < 65536, "16-bit offsets");
+  }
+  // one step's DMA instructions into staging slot st (LDS address); fp8 instruction j of
+  // this wave (0..3 codes, 4 rope, 5 scales on wave 0)
+  auto dma_f8 = [&](const StepRsrc& rs, uint32_t st, int j) {
+    if (j < 4) {
+      lds_dma_x4(st + 1024u * (uint32_t)(wave + 4 * j), (f8_dma & 0xFFFFu) + 8u * kF8Row * (uint32_t)j, rs.kv);
+    } else if (j == 4) {
+      lds_dma_x4(st + kR8StRope + 1024u * (uint32_t)wave, f8_dma >> 16, rs.kv);
+    } else if (wave == 0) {
+      lds_dma_x4(st + kR8StScales, lane < 32 ? 16u * (uint32_t)lane : 0x40000000u, rs.sc);
+    }
+  };
   auto issue_step = [&]() {
-    const i32x4 rs = lc.k <= k_last ? cursor_rsrc<false>(lc, a, kv_ptr, nullptr).kv
-                                    : make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
+    const StepRsrc rs = step_rsrc();
+    if constexpr (kFp8) {
+      const uint32_t st = lds_u32 + kR8StBase + (uint32_t)load_slot * kR8StBytes;
 #pragma unroll
-    for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + load_slot * kBufBytes, n, dma_voff(dmo, n), wave);
+      for (int j = 0; j < 6; ++j) dma_f8(rs, st, j);
+    } else {
+#pragma unroll
+      for (int n = 0; n < kR32Dma; ++n) issue32(rs.kv, lds_u32 + load_slot * kBufBytes, n, dma_voff(dmo, n), wave);
+    }
     advance();
+  };
+  // fp8 dequantisation of half h (tokens 16h .. 16h+15) of staging slot st into bf16 slot bs
+  // (LDS byte offsets): the lane's read and write bases, then per piece c
+  struct F8Half { uint32_t rd, wr; };
+  auto f8_half = [&](uint32_t st, uint32_t bs, int h) -> F8Half {
+    F8Half b;
+    b.rd = st + (f8_dq & 0xFFFFu) + (uint32_t)h * 16u * kLat;
+    b.wr = bs + (f8_dq >> 16) + (uint32_t)h * 16u * kRowBytes;
+    return b;
+  };
+  auto f8_scale = [&](uint32_t st, int h) -> float {
+    return *(const float __attribute__((address_space(3)))*)(lds + (st + (f8_aux & 0xFFFFu) + 256u * (uint32_t)h));
+  };
+  auto f8_codes = [&](const F8Half& b, int c) -> u32x2 {
+    return *(const u32x2 __attribute__((address_space(3)))*)(lds + (b.rd ^ (32u * (uint32_t)c)));
+  };
+  auto f8_store = [&](const F8Half& b, int c, bf16x4 lo, bf16x4 hi) {
+    *(bf16x8 __attribute__((address_space(3)))*)(lds + ((b.wr ^ (64u * (uint32_t)(c & 1))) + 128u * (uint32_t)(c >> 1))) =
+        __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto f8_rope = [&](uint32_t st) -> u32x4 {
+    return *(const u32x4 __attribute__((address_space(3)))*)(lds + (st + kR8StRope + 1024u * (uint32_t)wave +
+                                                                     16u * (uint32_t)lane));
+  };
+  auto f8_rope_store = [&](uint32_t bs, u32x4 v) {
+    *(u32x4 __attribute__((address_space(3)))*)(lds + (bs + (f8_aux >> 16))) = v;
+  };
+  // a whole step (start-up and redo passes only)
+  auto f8_dequant_step = [&](uint32_t st, uint32_t bs) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float sc = f8_scale(st, h);
+      const F8Half b = f8_half(st, bs, h);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x2 w = f8_codes(b, c);
+        f8_store(b, c, dequant4(w[0], sc), dequant4(w[1], sc));
+      }
+    }
+    f8_rope_store(bs, f8_rope(st));
+  };
+  // fp8: fill the pipeline from the cursor's step g0 in an empty ring: staging 0, 1, 2 <-
+  // steps g0 .. g0+2, bf16 slots 0, 1 <- steps g0, g0+1 dequantised, staging 0 <- step g0+3
+  // (in flight); on return every slot is visible and the next step loads into staging 1.
+  // That is the state every step region starts from: region i computes the values of step i
+  // and the scores of step i+1, dequantises step i+2 (staging slot) into the bf16 slot of
+  // step i, and loads step i+4.
+  auto f8_fill = [&]() {
+    issue_step();
+    issue_step();
+    issue_step();
+    wait_f8_steps<2>(wave);
+    barrier_lds();
+    f8_dequant_step(kR8StBase, 0);
+    wait_f8_steps<1>(wave);
+    barrier_lds();
+    issue_step();
+    f8_dequant_step(kR8StBase + kR8StBytes, kBufBytes);
+    wait_f8_steps<1>(wave);
+    barrier_lds();
   };
   // Start-up: the first item's 128 query rows (147 KB, contiguous in q) are staged through
   // the four ring slots by LDS-DMA, 32 rows per slot in the cache-step layout, and each wave
@@ -280,8 +438,12 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     q_item = kb;
     barrier_lds();   // every wave holds its rows before the ring is refilled
   }
+  if constexpr (kFp8) {
+    f8_fill();
+  } else {
 #pragma unroll 1
-  for (int i = 0; i < kR32Slots - 1; ++i) issue_step();
+    for (int i = 0; i < kR32Slots - 1; ++i) issue_step();
+  }
 
   int comp_slot = 0;   // ring slot of the segment's current step
 
@@ -323,6 +485,12 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       lim_min = __builtin_amdgcn_readfirstlane(m);
     }
     if (q_item != k) load_q(k);   // (after an item with no steps)
+    if constexpr (kFp8) {
+      // Q^T k-steps 34, 35 of the item to LDS (this wave's area; the score loops read them
+      // back there, which frees 8 VGPRs in the step loop)
+      *(bf16x8 __attribute__((address_space(3)))*)(lds + q_lds_addr(34)) = qreg[34];
+      *(bf16x8 __attribute__((address_space(3)))*)(lds + q_lds_addr(35)) = qreg[35];
+    }
 
     f32x16 o[16];
     float m_run = -INFINITY;   // reference max of the row (log2 domain, integer-valued once set)
@@ -420,7 +588,10 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       bf16x8 pcur[2];   // P of the current step for this wave's rows (A operands, k-steps 0, 1)
       bf16x8 bq0[4];    // Z^T of the current step's k-step 0, this wave's channel tiles (B operands)
       uint32_t zc = (uint32_t)comp_slot * kBufBytes;
-      wait_vmcnt<2 * kR32Dma>();   // data of step 0 (steps 1 and 2 may stay in flight)
+      // bf16: data of step 0 (steps 1 and 2 may stay in flight); fp8: steps 0 and 1 are in
+      // their bf16 slots since the last region or fill (the barrier orders the previous
+      // item's last LDS reads before the P writes below)
+      if constexpr (!kFp8) wait_vmcnt<2 * kR32Dma>();
       barrier_lds();
       // scores and softmax of step 0; its P goes to P buffer 0
       {
@@ -429,21 +600,25 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         const QkAddr qa = qk_at(qk0, zc);
 #pragma unroll
         for (int t = 0; t < kR32QkRing; ++t) qring[t] = qk_read(qa, t);
+        bf16x8 qx[2];
 #pragma unroll
         for (int t = 0; t < 36; ++t) {
           const bf16x8 cur = qring[t % kR32QkRing];
           if (t + kR32QkRing < 36) qring[t % kR32QkRing] = qk_read(qa, t + kR32QkRing);
+          if (kFp8 && t >= 30 && t < 32) qx[t - 30] = q_lds(t + 4);
           if (t == 0) mfma_v0(s, cur, qreg[0]);
-          else mfma_v(s, cur, qreg[t]);
+          else mfma_v(s, cur, (kFp8 && t >= 34) ? qx[t - 34] : qreg[t]);
         }
 #pragma unroll
         for (int p = 0; p < kPieces; ++p) softmax_piece(s, sg.hh0, true, p, pcur);
         p_store(0, pcur);
-        const PvAddr pa = pv_at(pv0, zc);
+        if constexpr (!kFp8) {   // (the fp8 step region reads its value operands itself)
+          const PvAddr pa = pv_at(pv0, zc);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) bq0[c] = pv_read(pa, c);
+          for (int c = 0; c < 4; ++c) bq0[c] = pv_read(pa, c);
+        }
       }
-      wait_vmcnt<kR32Dma>();      // data of step 1, for the first region's scores
+      if constexpr (!kFp8) wait_vmcnt<kR32Dma>();   // data of step 1, for the first region's scores
       barrier_lds();               // (and every wave's P of step 0)
 
       // Straight-line step body: the scores of step i+1 are computed also after the last
@@ -452,12 +627,37 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       // shape and the same DMA count.
 #pragma unroll 1
       for (int i = 0; i < nsteps; ++i) {
-        const int cs_next = comp_slot + 1 == kR32Slots ? 0 : comp_slot + 1;
+        const int cs_next = kFp8 ? comp_slot ^ 1 : (comp_slot + 1 == kR32Slots ? 0 : comp_slot + 1);
         const uint32_t zn = (uint32_t)cs_next * kBufBytes;
         const bool live = i + 1 < nsteps;   // step i+1 belongs to this segment
-        const i32x4 rs = lc.k <= k_last ? cursor_rsrc<false>(lc, a, kv_ptr, nullptr).kv
-                                        : make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
-        const uint32_t lslot = lds_u32 + (uint32_t)load_slot * kBufBytes;
+        const StepRsrc rs = step_rsrc();
+        const uint32_t lslot = kFp8 ? lds_u32 + kR8StBase + (uint32_t)load_slot * kR8StBytes
+                                    : lds_u32 + (uint32_t)load_slot * kBufBytes;
+        // fp8: the staged step i+2 (the slot after the one being loaded) is dequantised into
+        // the bf16 slot of step i, this wave's 128 channels: tokens 0..15 while the scores are
+        // computed (this wave read them before the last barrier), tokens 16..31 piece by
+        // piece after the value operand reads of step i (LDS executes a wave's accesses in
+        // order); the rope in the score phase (its last reader was the previous region)
+        const uint32_t st_dq = kR8StBase + (uint32_t)(load_slot + 1 == kR8Stage ? 0 : load_slot + 1) * kR8StBytes;
+        float f8_s = 0.f;
+        F8Half f8_b;
+        u32x2 f8_w[2];
+        bf16x4 f8_lo;
+        u32x4 f8_rp;
+        // piece q of the dequantisation of half h: q = 0 the scale and bases, 1 + c the codes
+        // of piece c, 5 + 2c the first 4 values of piece c, 6 + 2c the other 4 and the store
+        auto f8_piece = [&](int h, int q) {
+          if (q == 0) {
+            f8_s = f8_scale(st_dq, h);
+            f8_b = f8_half(st_dq, zc, h);
+          } else if (q <= 4) {
+            f8_w[(q - 1) & 1] = f8_codes(f8_b, q - 1);
+          } else {
+            const int c = (q - 5) >> 1;
+            if (((q - 5) & 1) == 0) f8_lo = dequant4(f8_w[c & 1][0], f8_s);
+            else f8_store(f8_b, c, f8_lo, dequant4(f8_w[c & 1][1], f8_s));
+          }
+        };
         const uint32_t pbuf = plane + (uint32_t)(i & 1) * kR32PBytes;   // P of step i (this lane)
         uint32_t voff = 0;        // source offset of the next DMA instruction (3 MFMAs ahead)
         f32x16 s;                 // scores of step i+1
@@ -467,6 +667,76 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
           const uint32_t rb = (uint32_t)((wave + g) & 3);
           return lds_b128(lds + (pbuf + rb * 2048u + (uint32_t)q * 1024u));
         };
+        if constexpr (kFp8) {
+          // 2) scores of step i+1 with the DMA instructions of step i+4 and half 0 of the
+          //    dequantisation of step i+2 between them. Half 0 overwrites the k-step-0 rows of
+          //    step i, so each Z^T tile of k-step 0 is read just before its piece is stored
+          //    (LDS executes a wave's accesses in order); the P tiles of k-step 0 are read
+          //    during the last score MFMAs
+          bf16x8 aq0[2], bz0[4];   // (P tiles of k-step 0: two in flight)
+          {
+            const PvAddr pa = pv_at(pv0, zc);
+            bf16x8 qring[kF8QkRing];
+            const QkAddr qa = qk_at(qk0, zn);
+#pragma unroll
+            for (int t = 0; t < kF8QkRing; ++t) qring[t] = qk_read(qa, t);
+            bf16x8 qx[2];
+#pragma unroll
+            for (int t = 0; t < 36; ++t) {
+              const bf16x8 cur = qring[t % kF8QkRing];
+              if (t + kF8QkRing < 36) qring[t % kF8QkRing] = qk_read(qa, t + kF8QkRing);
+              if (t >= 30 && t < 32) qx[t - 30] = q_lds(t + 4);
+              if (t == 33) aq0[0] = a_read(0, 0);
+              if (t >= 18 && t < 26 && !(t & 1)) bz0[(t - 18) >> 1] = pv_read(pa, (t - 18) >> 1);
+              if (t == 0) mfma_v0(s, cur, qreg[0]);
+              else mfma_v(s, cur, t >= 34 ? qx[t - 34] : qreg[t]);
+              if ((t & 3) == 3 && t < 24) dma_f8(rs, lslot, t >> 2);
+              if (t == 14) f8_piece(0, 0);
+              if (t == 15) f8_piece(0, 1);
+              if (t == 17) f8_piece(0, 2);
+              if (t >= 19 && t < 27) f8_piece(0, t - 14);   // codes two pieces ahead of their conversion
+              if (t == 20) f8_piece(0, 3);
+              if (t == 22) f8_piece(0, 4);
+              if (t == 8) f8_rp = f8_rope(st_dq);
+              if (t == 11) f8_rope_store(zc, f8_rp);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          // 3) the 32 value MFMAs of step i (k-step 0 row block by row block, then k-step 1
+          //    channel tile by channel tile) with the softmax of step i+1 and half 1 of the
+          //    dequantisation between them (its stores after the last Z^T read of step i)
+          {
+            const PvAddr pa = pv_at(pv0, zc);
+            bf16x8 bq1[3];   // ring of Z^T tiles of k-step 1
+            bf16x8 aq1[4];   // P tiles of k-step 1
+#pragma unroll
+            for (int t = 0; t < 32; ++t) {
+              if (t == 6) bq1[0] = pv_read(pa, 16 + 0);
+              if (t >= 8 && t < 12) aq1[t - 8] = a_read(t - 8, 1);
+              if (t == 12) bq1[1] = pv_read(pa, 16 + 1);
+              if (t == 16) bq1[2] = pv_read(pa, 16 + 2);
+              if (t == 20) bq1[0] = pv_read(pa, 16 + 3);
+              if (t < 12 && t % 4 == 1) aq0[((t + 3) / 4) & 1] = a_read((t + 3) / 4, 0);
+              if (t < 16) {
+                const int g = t / 4, c = t % 4;
+                mfma_a(o[4 * g + c], aq0[g & 1], bz0[c]);
+              } else {
+                const int c = (t - 16) / 4, g = (t - 16) % 4;
+                mfma_a(o[4 * g + c], aq1[g], bq1[c % 3]);
+              }
+              if (t < kPieces) softmax_piece(s, sg.hh0 + i + 1, live, t, pnext);
+              if (t == 22) f8_piece(1, 0);
+              if (t == 23) f8_piece(1, 1);
+              if (t == 24) f8_piece(1, 2);
+              if (t >= 25) f8_piece(1, t - 20);
+              if (t == 26) f8_piece(1, 3);
+              if (t == 28) f8_piece(1, 4);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          f8_piece(1, 12);
+          p_store((i + 1) & 1, pnext);
+        } else {
         // 1) the first value MFMAs of step i: this wave's rows, k-step 0, its four channel
         //    tiles (operands in registers)
 #pragma unroll
@@ -492,7 +762,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
             if (t == 0) mfma_v0(s, cur, qreg[0]);
             else mfma_v(s, cur, qreg[t]);
             if ((t & 3) == 0) voff = dma_voff(dmo, t >> 2);   // offset of the next DMA instruction
-            if ((t & 3) == 3) issue32(rs, lslot, t >> 2, voff, wave);
+            if ((t & 3) == 3) issue32(rs.kv, lslot, t >> 2, voff, wave);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -534,10 +804,13 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
 #pragma unroll
           for (int c = 0; c < 4; ++c) bq0[c] = pv_read(pa, c);
         }
+        }
         // move the load cursor here: its scalar loads share the LDS counter, and the barrier
         // waits for that counter anyway
         advance();
-        wait_vmcnt<kR32Dma>();   // everything but this region's DMA: the data of step i+2
+        // everything but this region's DMA: the data of step i+2 (bf16) or i+3 (fp8)
+        if constexpr (kFp8) wait_f8_steps<1>(wave);
+        else wait_vmcnt<kR32Dma>();
         barrier_lds();
         comp_slot = cs_next;
         zc = zn;
@@ -546,7 +819,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       // Did any row of the work-group leave the reference window? (vote through LDS)
       {
         int32_t __attribute__((address_space(3)))* vote =
-            (int32_t __attribute__((address_space(3)))*)(lds + kR32Votes);
+            (int32_t __attribute__((address_space(3)))*)(lds + kPBase);
         // (a NaN sum counts as out of range)
         const bool lane_bad = track ? window_exceeded : !(l_run <= 0x1p60f);
         const bool wave_exceeded = __ballot(lane_bad) != 0;   // (all lanes take part)
@@ -578,8 +851,12 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
       load_slot = 0;
       comp_slot = 0;
+      if constexpr (kFp8) {
+        f8_fill();
+      } else {
 #pragma unroll 1
-      for (int j = 0; j < kR32Slots - 1; ++j) issue_step();
+        for (int j = 0; j < kR32Slots - 1; ++j) issue_step();
+      }
     }
 
     // ---- finalize: out = O / l and lse = m + log2(l), or, for items the plan split, the
@@ -595,7 +872,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       const bool split = itf[kINsplits] > 1;
       const int slot = split ? itf[kISlot] + (worker - itf[kIOwner]) : 0;
       const int row0 = kRowsPerTile * f_tile + 32 * wave;   // the first row this wave owns
-      float __attribute__((address_space(3)))* inv_s = (float __attribute__((address_space(3)))*)(lds + kR32InvL);
+      float __attribute__((address_space(3)))* inv_s = (float __attribute__((address_space(3)))*)(lds + kPBase + 64);
       if (!split) {
         if (l < 32) inv_s[32 * wave + l] = l_run > 0.f ? 1.f / l_run : 0.f;
         barrier_lds();   // every row's 1/l from the wave that owns it
@@ -814,23 +1091,29 @@ __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode_rows32(const DecodeArgs& a, hipStream_t stream) {
+template <bool kFp8>
+hipError_t launch_rows32(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int lds_bytes = kFp8 ? kR8LdsTotal : kR32LdsTotal;
   static thread_local int configured = -1;   // the LDS opt-in is per device
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (configured != dev) {
-    e = hipFuncSetAttribute((const void*)decode_rows32_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kR32LdsTotal);
+    e = hipFuncSetAttribute((const void*)decode_rows32_kernel<kFp8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            lds_bytes);
     if (e != hipSuccess) return e;
     configured = dev;
   }
-  hipLaunchKernelGGL(decode_rows32_kernel, dim3(a.workers), dim3(kR32Threads), kR32LdsTotal, stream,
-                     reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const char*>(a.kv), a.block_table,
-                     a.seqlens, a.plan, a.ws, a.out, a.lse, scalars_of(a));
+  hipLaunchKernelGGL(decode_rows32_kernel<kFp8>, dim3(a.workers), dim3(kR32Threads), lds_bytes, stream,
+                     reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const char*>(a.kv), a.kv_scales,
+                     a.block_table, a.plan, a.ws, a.out, a.lse, scalars_of(a));
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_rows32(const DecodeArgs& a, bool fp8, hipStream_t stream) {
+  return fp8 ? launch_rows32<true>(a, stream) : launch_rows32<false>(a, stream);
 }
 
 hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream) {

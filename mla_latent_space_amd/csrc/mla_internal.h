@@ -79,7 +79,7 @@ struct DecodeArgs {
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_rows32(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_rows32(const DecodeArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int tokens, int heads,
                                void* qz, hipStream_t stream);

@@ -14,9 +14,12 @@ import mla_latent_space_amd as mla
 # softmax_scale * 2^-8 * sum_c |q_c z_c| (about 1e-1 in the worst case and 6e-3 typical for
 # these N(0,1) draws, whose per-value errors have random signs); lse moves by no more than
 # the largest score error, so fp8 lse is held to 2e-2, about three times the typical
-# perturbation, and max abs keeps the bf16 bound.
+# perturbation. out = sum_u p_u z_u with sum_u p_u = 1, and both z_u (the dequantised value)
+# and p_u are rounded once to bf16, so |d out_c| <= 2 * 2^-8 * max_u |z_uc| besides the
+# score term; the latent values of these workloads stay below 5 in magnitude, which gives
+# max abs <= 4e-2 (reached only by rows with a handful of visible keys).
 BF16_TOL = dict(rel_l2=5e-3, max_abs=2e-2, lse=1e-3)
-FP8_TOL = dict(rel_l2=3e-2, max_abs=2e-2, lse=2e-2)
+FP8_TOL = dict(rel_l2=3e-2, max_abs=4e-2, lse=2e-2)
 
 
 class Dev:
