@@ -56,7 +56,7 @@ def describe(w) -> str:
 
 
 # kernel sources whose sha256 keys the committed HBM-traffic record
-TRAFFIC_SOURCES = ("mla_device.h", "mla_decode.hip", "mla_decode_rows32.hip", "mla_plan.hip")
+TRAFFIC_SOURCES = ("mla_device.h", "mla_decode_rows32.hip", "mla_plan.hip")
 
 
 def traffic_from_profile(kernel_srcs, key):

@@ -25,12 +25,7 @@ constexpr int kDmaInstr = kBufBytes / 1024;    // 36 LDS-DMA instructions (1 KiB
 // fp8 cache (OCP e4m3fn): a cached row is 512 codes + 64 bf16 rope channels (640 B), with
 // one f32 scale per 128-channel tile of the 512 latent channels in a separate array.
 constexpr int kF8Row = kLat + 2 * kRope;       // 640
-constexpr int kF8StepBytes = kStep * kF8Row;   // 20480: a half page of codes+rope, contiguous
-constexpr int kF8SlotBytes = kF8StepBytes + kStep * 16;   // + the step's 32 x 4 scales
-constexpr int kF8Slots = 3;                    // fp8 staging ring depth
-constexpr int kF8DmaInstr = kF8StepBytes / 1024 + 1;      // 20 row instructions + 1 for the scales
 
-constexpr float kTau = 8.0f;                   // lazy rescale threshold (log2 units)
 constexpr uint32_t kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit format, gfx9 family
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14)

@@ -12,8 +12,6 @@ constexpr int kDqk = kLat + kRope; // 576: absorbed query / cached row width
 constexpr int kNope = 128;         // per-head query channels before absorption
 constexpr int kDv = 128;           // per-head value channels after decompression
 constexpr int kRowsPerTile = 128;  // query rows (token, head) per work item
-constexpr int kFp8RowBytes = kLat + 2 * kRope;  // 640
-constexpr int kFp8Tiles = kLat / 128;           // 4 scales per token
 
 // Planner limits.
 constexpr int kMaxItems = 16384;
@@ -50,10 +48,10 @@ __host__ __device__ inline int tiles_per_seq(int s_q, int heads) {
   return (s_q * heads + kRowsPerTile - 1) / kRowsPerTile;
 }
 
-// Workspace: per partial slot (one split part of a 128-row item), the partial out as bf16 in
-// the value MFMAs' register order (128 x 512 values, see the decode kernels' finalize), then
-// two fp32 per row: bf16 cache kernel: the unnormalised partial's reference max (log2 units)
-// and its softmax denominator; fp8 cache kernel: a normalised partial's lse (first half).
+// Workspace: per partial slot (one split part of a 128-row item), the unnormalised partial out
+// as bf16 in the value MFMAs' register order (128 x 512 values, see the decode kernel's
+// finalize), then two fp32 per row: its reference max (log2 units) and its softmax
+// denominator.
 constexpr int64_t kSlotPartBytes = (int64_t)kRowsPerTile * kLat * 2;
 constexpr int64_t kSlotBytes = kSlotPartBytes + (int64_t)kRowsPerTile * 8;
 
@@ -77,8 +75,6 @@ struct DecodeArgs {
   float* lse;
 };
 
-hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_rows32(const DecodeArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int tokens, int heads,
