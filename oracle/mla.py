@@ -12,6 +12,8 @@ Definitions followed (page "Mla Analysis", skillmd.com):
   576-wide concatenation [Z | KPE] and an absorbed query is [q_nope W_k^T | q_rope].
 * Section "Cost Models": FLOP and byte models of FlashAttention, FlashMLA and
   MLAvar6+.
+* Section "MLAvar6+ Design": o old tokens as latent rows, n new tokens decompressed,
+  t = o + n; the attention over their union is exact.
 
 FlashMLA-2 newsletter page, section "Architectural Analysis": the latent cache may be
 stored in FP8 and scaled up before the matrix products; OCP e4m3fn is the format read
@@ -179,6 +181,43 @@ def decode_explicit(q_nope: np.ndarray, q_rope: np.ndarray, w_k: np.ndarray, w_v
         v_eta = z[:, :K_LAT] @ w_v[eta]
         q_eta = np.concatenate([q_nope[eta], q_rope[eta]])[None, :]
         o, l = softmax_attention(q_eta, k_eta, v_eta, scale)
+        out[eta] = o[0]
+        lse[eta] = l[0]
+    return out, lse
+
+
+def hybrid_visible_new(n: int, s_q: int, j: int, causal: bool) -> int:
+    """Split latent + decompressed variant (section "MLAvar6+ Design"): the n newest of a
+    sequence's t tokens are the decompressed ones. Under the causal reading query j sees keys
+    0 .. t - s + j, i.e. every old token and the first n - s + 1 + j new ones (n >= s)."""
+    if not causal:
+        return int(n)
+    if n < s_q:
+        raise ValueError("the causal split needs n >= s_q (the old tokens must all be visible)")
+    return int(n - s_q + 1 + j)
+
+
+def decode_hybrid(q_nope: np.ndarray, q_rope: np.ndarray, w_k: np.ndarray, w_v: np.ndarray,
+                  z_old: np.ndarray, k_new: np.ndarray, kr_new: np.ndarray, v_new: np.ndarray,
+                  scale: float, vis_new: int):
+    """Page "Mla Analysis", section "MLAvar6+ Design": the cache of one sequence is split into
+    o old tokens kept as latent rows Z [o, k + p] and n new tokens kept decompressed (K [n, h, d]
+    and V [n, h, d], with the shared rope key KPE [n, p]). The attention is the same softmax over
+    all of them: for head h the keys are [Z[:, :k] W_k,h | Z[:, k:]] (old) and [K_h | KPE] (new),
+    the values Z[:, :k] W_v,h (old) and V_h (new). One query token; the new tokens visible are
+    the first ``vis_new``. Returns O [h, d] and lse [h]."""
+    h = q_nope.shape[0]
+    d = w_v.shape[2]
+    out = np.empty((h, d))
+    lse = np.empty(h)
+    for eta in range(h):
+        k_old = np.concatenate([z_old[:, :K_LAT] @ w_k[eta], z_old[:, K_LAT:]], axis=1)
+        v_old = z_old[:, :K_LAT] @ w_v[eta]
+        k_n = np.concatenate([k_new[:vis_new, eta], kr_new[:vis_new]], axis=1)
+        v_n = v_new[:vis_new, eta]
+        q_eta = np.concatenate([q_nope[eta], q_rope[eta]])[None, :]
+        o, l = softmax_attention(q_eta, np.concatenate([k_old, k_n], axis=0),
+                                 np.concatenate([v_old, v_n], axis=0), scale)
         out[eta] = o[0]
         lse[eta] = l[0]
     return out, lse
