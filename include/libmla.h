@@ -181,6 +181,39 @@ int32_t mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_k
 int32_t mla_decompress_output(const float* out_latent, const void* w_v, int32_t tokens, int32_t heads,
                               float* out, void* stream);
 
+/* Split latent + decompressed attention (page "Mla Analysis", section "MLAvar6+ Design"): a
+ * sequence's t cached tokens are split into o old tokens kept as latent rows and its n newest
+ * kept decompressed (per head K and V of 128 channels, with the shared 64-channel rope key).
+ * The old part is computed by mla_decode_fwd over the o latent tokens (seqlens = o, causal =
+ * 0) followed by mla_decompress_output; this call attends over the n new tokens and merges the
+ * two parts by their log-sum-exps, so that the result is the softmax attention over all t
+ * tokens. Per query row (sequence i, token j, head e), with the new tokens visible to it
+ * (all n; with causal, the first n - s_q + 1 + j, which keeps every old token visible):
+ *
+ *     a_u  = softmax_scale * ([q_nope | q_rope] . [k_new[i, u, e] | kr_new[i, u]])
+ *     lse  = log(exp(lse_old) + sum_u exp(a_u))                  (natural log)
+ *     out  = (exp(lse_old) out_old + sum_u exp(a_u) v_new[i, u, e]) / exp(lse)
+ *
+ * lse_old = -inf (an empty old part) and n_new = 0 are allowed; no key at all gives out = 0,
+ * lse = -inf.
+ *
+ * q_nope   device bf16 [batch, s_q, heads, 128]; q_rope device bf16 [batch, s_q, heads, 64]
+ *          (the unabsorbed query, rope rotation applied).
+ * k_new    device bf16 [batch, n_new, heads, 128]; kr_new device bf16 [batch, n_new, 64];
+ *          v_new device bf16 [batch, n_new, heads, 128]: the new tokens, oldest first (the
+ *          last n_new of every sequence). May be NULL when n_new = 0.
+ * out_old  device float32 [batch, s_q, heads, 128]: the old part's normalised output (the
+ *          decompressed out of mla_decode_fwd); lse_old device float32 [batch, s_q, heads].
+ * out      device float32 [batch, s_q, heads, 128]; lse device float32 [batch, s_q, heads].
+ * batch, heads 1 .. 65535; s_q 1 .. 32; n_new 0 .. 2^24; with causal, n_new >= s_q.
+ * softmax_scale finite and > 0. All arrays but the lse ones 16-byte aligned and contiguous.
+ * Stream-ordered; allocates nothing. Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
+ * MLA_ERR_HIP. */
+int32_t mla_hybrid_merge(const void* q_nope, const void* q_rope, const void* k_new, const void* kr_new,
+                         const void* v_new, int32_t n_new, const float* out_old, const float* lse_old,
+                         int32_t batch, int32_t s_q, int32_t heads, float softmax_scale, int32_t causal,
+                         float* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

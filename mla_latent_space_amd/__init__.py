@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["MlaError", "SplitPlan", "lib", "abi_version", "default_num_workers", "plan_bytes", "workspace_bytes",
            "absorb_query", "decompress_output",
-           "get_split_plan", "decode_fwd", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3"]
+           "get_split_plan", "decode_fwd", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3", "hybrid_merge"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 KV_BF16 = 0
@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
     L.mla_absorb_query.argtypes = [c_p, c_p, c_p, c_i32, c_i32, c_p, c_p]
     L.mla_decompress_output.restype = c_i32
     L.mla_decompress_output.argtypes = [c_p, c_p, c_i32, c_i32, c_p, c_p]
+    L.mla_hybrid_merge.restype = c_i32
+    L.mla_hybrid_merge.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_f, c_i32, c_p,
+                                   c_p, c_p]
     _lib = L
     return L
 
@@ -220,3 +223,34 @@ def decompress_output(out_latent: torch.Tensor, w_v: torch.Tensor,
     _check(int(lib().mla_decompress_output(out_latent.data_ptr(), w_v.data_ptr(), tokens, heads, out.data_ptr(),
                                            _stream(out_latent))))
     return out
+
+
+def hybrid_merge(q_nope: torch.Tensor, q_rope: torch.Tensor, k_new: Optional[torch.Tensor],
+                 kr_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor], out_old: torch.Tensor,
+                 lse_old: torch.Tensor, softmax_scale: float, causal: bool = False,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """The new tokens' attention merged with the old part (see mla_hybrid_merge). q_nope bf16
+    [b, s, h, 128], q_rope bf16 [b, s, h, 64]; k_new, v_new bf16 [b, n, h, 128] and kr_new bf16
+    [b, n, 64] (None with n = 0); out_old float32 [b, s, h, 128], lse_old float32 [b, s, h].
+    Returns (out float32 [b, s, h, 128], lse float32 [b, s, h])."""
+    b, s_q, heads = int(q_nope.shape[0]), int(q_nope.shape[1]), int(q_nope.shape[2])
+    _need(q_nope, "q_nope", torch.bfloat16, (b, s_q, heads, 128))
+    _need(q_rope, "q_rope", torch.bfloat16, (b, s_q, heads, 64))
+    n = 0 if k_new is None else int(k_new.shape[1])
+    if n > 0:
+        _need(k_new, "k_new", torch.bfloat16, (b, n, heads, 128))
+        _need(kr_new, "kr_new", torch.bfloat16, (b, n, 64))
+        _need(v_new, "v_new", torch.bfloat16, (b, n, heads, 128))
+    _need(out_old, "out_old", torch.float32, (b, s_q, heads, 128))
+    _need(lse_old, "lse_old", torch.float32, (b, s_q, heads))
+    if out is None:
+        out = torch.empty((b, s_q, heads, 128), dtype=torch.float32, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((b, s_q, heads), dtype=torch.float32, device=q_nope.device)
+    _need(out, "out", torch.float32, (b, s_q, heads, 128))
+    _need(lse, "lse", torch.float32, (b, s_q, heads))
+    ptr = (lambda t: t.data_ptr() if t is not None and n > 0 else None)
+    _check(int(lib().mla_hybrid_merge(q_nope.data_ptr(), q_rope.data_ptr(), ptr(k_new), ptr(kr_new), ptr(v_new), n,
+                                      out_old.data_ptr(), lse_old.data_ptr(), b, s_q, heads, float(softmax_scale),
+                                      1 if causal else 0, out.data_ptr(), lse.data_ptr(), _stream(q_nope))))
+    return out, lse

@@ -206,4 +206,49 @@ int32_t mla_decompress_output(const float* out_latent, const void* w_v, int32_t 
   return ok();
 }
 
+int32_t mla_hybrid_merge(const void* q_nope, const void* q_rope, const void* k_new, const void* kr_new,
+                         const void* v_new, int32_t n_new, const float* out_old, const float* lse_old, int32_t batch,
+                         int32_t s_q, int32_t heads, float softmax_scale, int32_t causal, float* out, float* lse,
+                         void* stream) {
+  if (!q_nope || !q_rope || !out_old || !lse_old || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL (q_nope, q_rope, out_old, lse_old, out, lse)");
+  if (n_new < 0) return fail(MLA_ERR_INVALID_ARG, "n_new must be >= 0 (got %d)", n_new);
+  if (n_new > 0 && (!k_new || !kr_new || !v_new))
+    return fail(MLA_ERR_INVALID_ARG, "k_new, kr_new and v_new are required when n_new > 0");
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (s_q < 1) return fail(MLA_ERR_INVALID_ARG, "s_q must be >= 1 (got %d)", s_q);
+  if (heads < 1) return fail(MLA_ERR_INVALID_ARG, "heads must be >= 1 (got %d)", heads);
+  if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (s_q > 32) return fail(MLA_ERR_UNSUPPORTED, "s_q must be <= 32 (got %d)", s_q);
+  if (batch > 65535 || heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch and heads must be <= 65535");
+  if (n_new > (1 << 24)) return fail(MLA_ERR_UNSUPPORTED, "n_new must be <= 2^24 (got %d)", n_new);
+  if (causal && n_new < s_q)
+    return fail(MLA_ERR_UNSUPPORTED, "causal needs n_new >= s_q (got n_new %d, s_q %d): the old tokens must all "
+                "be visible", n_new, s_q);
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(out_old) || !aligned16(out) ||
+      (n_new > 0 && (!aligned16(k_new) || !aligned16(kr_new) || !aligned16(v_new))))
+    return fail(MLA_ERR_INVALID_ARG, "q_nope, q_rope, k_new, kr_new, v_new, out_old and out must be 16-byte aligned");
+  mla::HybridArgs a;
+  a.q_nope = q_nope;
+  a.q_rope = q_rope;
+  a.k_new = k_new;
+  a.kr_new = kr_new;
+  a.v_new = v_new;
+  a.out_old = out_old;
+  a.lse_old = lse_old;
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.s_q = s_q;
+  a.heads = heads;
+  a.n_new = n_new;
+  a.causal = causal;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipError_t e = mla::launch_hybrid_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hybrid merge kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

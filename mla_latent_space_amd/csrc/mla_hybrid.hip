@@ -1,0 +1,273 @@
+// Split latent + decompressed attention (page "Mla Analysis", section "MLAvar6+ Design"): a
+// sequence's o old tokens are latent rows, handled by the latent decode and the output
+// decompression, and its n newest tokens are kept decompressed, per head K [n, h, 128] and
+// V [n, h, 128] plus the shared rope key [n, 64]. This kernel attends over the new tokens and
+// merges the result with the old part's (out, lse) by their log-sum-exps, which makes the
+// softmax span all t = o + n tokens exactly.
+//
+// One work-group of four waves per (sequence, head); all s_q <= 32 query rows of the head form
+// one 32-row MFMA tile (rows past s_q repeat row 0 and are not written). Wave w takes the new
+// tokens' 32-token chunks w, w+4, ...: the chunk's K rows (128 + 64 channels, 384 B) and V rows
+// are loaded into registers while the previous chunk is computed, then stored in the wave's
+// LDS area as 384-B rows with 16-B chunks XOR-swizzled by token, the layout whose operand reads
+// are free of bank conflicts. Per chunk: S^T[32 tokens x 32 rows] = K Q^T (12
+// v_mfma_f32_32x32x16_bf16, Q^T in registers), mask, online softmax in the log2 domain with a
+// reference that moves only when a row's maximum passes it by more than 2^8, then
+// O[32 rows x 128] += P V (8 MFMAs; P is the score accumulator rounded to bf16, read as the A
+// operand with its token order, V^T tiles from transposing LDS reads). The four waves' partials
+// and the old part are then merged through LDS. The new tokens' part moves w(2 h n d + n p)
+// bytes for 4 h s n d flops per sequence, far below the MI355X ridge: it is bound by HBM.
+#include "mla_device.h"
+
+namespace mla {
+namespace {
+
+constexpr int kHyThreads = 256;
+constexpr int kHyChunk = 32;                     // new tokens per chunk
+constexpr int kHyRow = 384;                      // LDS row: 128 + 64 channels of K (or 128 of V + pad)
+constexpr int kHyArea = 2 * kHyChunk * kHyRow;   // per wave: K rows, then V rows (24 KiB)
+constexpr int kHyAlpha = 4 * kHyArea;            // per wave: 32 rescale factors
+constexpr int kHyLds = kHyAlpha + 4 * 32 * 4;
+constexpr int kHyLoads = 20;                     // 16-B loads per lane and chunk: 12 of K, 8 of V
+static_assert(kHyRow % 256 == 128, "consecutive tokens alternate 128-B bank halves");
+constexpr int kHyObufRow = 160;                  // floats per partial O row in the merge (640 B)
+static_assert(4 * 32 * kHyObufRow * 4 + 4 * 32 * 8 <= kHyAlpha, "the merge area fits in the staging areas");
+
+__device__ __forceinline__ uint32_t hy_sw(uint32_t u) { return (((u >> 1) & 1u) << 2) | ((u >> 2) & 3u); }
+// LDS byte offset of logical 16-B chunk ch of token row u
+__device__ __forceinline__ uint32_t hy_pos(uint32_t u, uint32_t ch) {
+  return u * kHyRow + 16u * ((ch & ~7u) | ((ch & 7u) ^ hy_sw(u)));
+}
+
+__global__ __launch_bounds__(kHyThreads, 1) void hybrid_new_kernel(
+    const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_rope, const __bf16* __restrict__ k_new,
+    const __bf16* __restrict__ kr_new, const __bf16* __restrict__ v_new, const float* __restrict__ out_old,
+    const float* __restrict__ lse_old, float* __restrict__ out, float* __restrict__ lse, int S, int N, int H,
+    float scale_log2, int causal) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  char __attribute__((address_space(3)))* lds = (char __attribute__((address_space(3)))*)smem_raw;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t kbase = (uint32_t)wave * kHyArea, vbase = kbase + kHyChunk * kHyRow;
+  const int row = lane & 31, hl = lane >> 5;
+
+  // Q^T B operand: lane holds query row l%32, channels 16ks + 8(l/32) .. +7 (ks 0..7 nope, 8..11 rope)
+  bf16x8 qb[12];
+  {
+    const int j = row < S ? row : 0;
+    const __bf16* qn = q_nope + (((int64_t)b * S + j) * H + h) * 128 + 8 * hl;
+    const __bf16* qr = q_rope + (((int64_t)b * S + j) * H + h) * 64 + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qn + 16 * ks);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[8 + ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+  }
+  // new tokens visible to this lane's row (0 for padding rows)
+  const int lim = row < S ? (causal ? N - S + 1 + row : N) : 0;
+
+  // chunk loads: piece p = 64m + lane; K: token p / 24, chunk p % 24 (0..15 nope, 16..23 rope);
+  // V: token p / 16, chunk p % 16. Tokens past N read as zeros.
+  u32x4 st[kHyLoads];
+  auto load_chunk = [&](int c) {
+    const int tok0 = kHyChunk * c;
+#pragma unroll
+    for (int m = 0; m < 12; ++m) {
+      const int p = 64 * m + lane, tk = p / 24, ch = p % 24, u = tok0 + tk;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (u < N) {
+        const __bf16* src = ch < 16 ? k_new + (((int64_t)b * N + u) * H + h) * 128 + 8 * ch
+                                    : kr_new + ((int64_t)b * N + u) * 64 + 8 * (ch - 16);
+        v = *reinterpret_cast<const u32x4*>(src);
+      }
+      st[m] = v;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int p = 64 * m + lane, tk = p / 16, ch = p % 16, u = tok0 + tk;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (u < N) v = *reinterpret_cast<const u32x4*>(v_new + (((int64_t)b * N + u) * H + h) * 128 + 8 * ch);
+      st[12 + m] = v;
+    }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int m = 0; m < 12; ++m) {
+      const int p = 64 * m + lane;
+      *(u32x4 __attribute__((address_space(3)))*)(lds + (kbase + hy_pos(p / 24, p % 24))) = st[m];
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int p = 64 * m + lane;
+      *(u32x4 __attribute__((address_space(3)))*)(lds + (vbase + hy_pos(p / 16, p % 16))) = st[12 + m];
+    }
+  };
+  // operand reads: K rows (lane: token l%32, logical chunk 2ks + l/32); V^T tile (q, c): tokens
+  // 16q + 8e + 4(G/2) + j/4 and channels 32c + 16(G%2) + 4(j%4) .. +3 for lane (G, j) = (l/16, l%16)
+  auto k_read = [&](int ks) -> bf16x8 {
+    return lds_b128(lds + (kbase + hy_pos((uint32_t)row, (uint32_t)(2 * ks + hl))));
+  };
+  auto v_read = [&](int q, int c) -> bf16x8 {
+    const uint32_t G = (uint32_t)lane >> 4, j = (uint32_t)lane & 15u;
+    bf16x4 part[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t u = 16u * q + 8u * e + 4u * (G >> 1) + (j >> 2);
+      const uint32_t ch = 4u * c + 2u * (G & 1u) + ((j >> 1) & 1u);
+      part[e] = lds_tr16(lds + (vbase + hy_pos(u, ch) + 8u * (j & 1u)));
+    }
+    return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = f32x16{};
+  float m_ref = -INFINITY;   // the row's reference (log2 units): p = 2^(s - m_ref)
+  float l_run = 0.f;
+  const int nchunks = (N + kHyChunk - 1) / kHyChunk;
+  bool first = true;
+  float __attribute__((address_space(3)))* alpha_s =
+      (float __attribute__((address_space(3)))*)(lds + kHyAlpha + 128 * wave);
+  if (wave < nchunks) load_chunk(wave);
+#pragma unroll 1
+  for (int c = wave; c < nchunks; c += 4) {
+    store_chunk();   // (after this wave's reads of the previous chunk: LDS keeps a wave's order)
+    if (c + 4 < nchunks) load_chunk(c + 4);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_read(ks), qb[ks], s, 0, 0, 0);
+    // mask (register r: token 32c + 8(r/4) + 4(l/32) + r%4) and the row maximum
+    const int key0 = kHyChunk * c + 4 * hl;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = (key0 + 8 * (r >> 2) + (r & 3)) < lim ? s[r] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[r]);
+    }
+    {
+      const unsigned u = __float_as_uint(mx);
+      const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // move the reference when the row maximum passes it by more than 2^8
+    const bool move = mx > m_ref + 8.f;
+    const float new_ref = move ? mx : m_ref;
+    const float alpha = move ? (m_ref == -INFINITY ? 0.f : exp2f(m_ref - new_ref)) : 1.f;
+    if (__ballot(move) != 0) {   // (wave-uniform)
+      l_run *= alpha;
+      if (!first) {   // O rows live in other lanes: their factors go through LDS
+        if (lane < 32) alpha_s[lane] = alpha;
+        f32x4 a4[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          a4[jj] = *(const f32x4 __attribute__((address_space(3)))*)(alpha_s + 8 * jj + 4 * hl);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[t][r] *= a4[r >> 2][r & 3];
+      }
+    }
+    m_ref = new_ref;
+    first = false;
+    const float muse = m_ref == -INFINITY ? 0.f : m_ref;
+    bf16x8 pk[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2f(s[r] - muse);
+      ps += p;
+      pk[r >> 3][r & 7] = (__bf16)p;
+    }
+    {
+      const unsigned u = __float_as_uint(ps);
+      const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      l_run += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pk[q], v_read(q, t), o[t], 0, 0, 0);
+  }
+
+  // ---- merge: the four waves' partials (relative to their references) and the old part
+  __syncthreads();   // every wave is done with its staging area
+  // partial O rows at a 640-B stride (128-B bank halves alternate), then the per-row (m, l)
+  float __attribute__((address_space(3)))* obuf = (float __attribute__((address_space(3)))*)lds;
+  float __attribute__((address_space(3)))* stat = obuf + 4 * 32 * kHyObufRow;
+  if (lane < 32) {
+    stat[2 * (32 * wave + row)] = m_ref;
+    stat[2 * (32 * wave + row) + 1] = l_run;
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = 8 * (r >> 2) + 4 * hl + (r & 3);
+      obuf[(32 * wave + rr) * kHyObufRow + 32 * t + row] = o[t][r];
+    }
+  __syncthreads();
+  {
+    // thread: row tid / 8, channels 32k + 4(tid % 8) .. +3 for k = 0..3
+    const int tid = threadIdx.x, rr = tid >> 3, q4 = 4 * (tid & 7);
+    if (rr < S) {
+      const int64_t orow = ((int64_t)b * S + rr) * H + h;
+      const float lo = lse_old[orow];
+      const float m_old = lo == -INFINITY ? -INFINITY : lo * 1.4426950408889634f;
+      float M = m_old;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, stat[2 * (32 * w + rr)]);
+      float a[4], den = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = stat[2 * (32 * w + rr)];
+        a[w] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        den += a[w] * stat[2 * (32 * w + rr) + 1];
+      }
+      const float a_old = (m_old == -INFINITY) ? 0.f : exp2f(m_old - M);
+      den += a_old;
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c0 = 32 * k + q4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (a_old != 0.f) {
+          const f32x4 ov = *reinterpret_cast<const f32x4*>(out_old + orow * 128 + c0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = a_old * ov[e];
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f32x4 pv = *(const f32x4 __attribute__((address_space(3)))*)(obuf + (32 * w + rr) * kHyObufRow + c0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += a[w] * pv[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= inv;
+        *reinterpret_cast<f32x4*>(out + orow * 128 + c0) = acc;
+      }
+      if ((tid & 7) == 0) lse[orow] = den > 0.f ? (M + __log2f(den)) * 0.6931471805599453f : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_hybrid_merge(const HybridArgs& a, hipStream_t stream) {
+  static thread_local int configured = -1;   // the LDS opt-in is per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (configured != dev) {
+    e = hipFuncSetAttribute((const void*)hybrid_new_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kHyLds);
+    if (e != hipSuccess) return e;
+    configured = dev;
+  }
+  hipLaunchKernelGGL(hybrid_new_kernel, dim3(a.heads, a.batch), dim3(kHyThreads), kHyLds, stream,
+                     static_cast<const __bf16*>(a.q_nope), static_cast<const __bf16*>(a.q_rope),
+                     static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.kr_new),
+                     static_cast<const __bf16*>(a.v_new), a.out_old, a.lse_old, a.out, a.lse, a.s_q, a.n_new,
+                     a.heads, a.scale_log2, a.causal);
+  return hipGetLastError();
+}
+
+}  // namespace mla

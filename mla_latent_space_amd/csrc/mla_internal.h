@@ -77,6 +77,14 @@ struct DecodeArgs {
 
 hipError_t launch_decode_rows32(const DecodeArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream);
+struct HybridArgs {
+  const void *q_nope, *q_rope, *k_new, *kr_new, *v_new;
+  const float *out_old, *lse_old;
+  float *out, *lse;
+  int batch, s_q, heads, n_new, causal;
+  float scale_log2;   // softmax_scale * log2(e)
+};
+hipError_t launch_hybrid_merge(const HybridArgs& a, hipStream_t stream);
 hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int tokens, int heads,
                                void* qz, hipStream_t stream);
 hipError_t launch_decompress_output(const float* out_latent, const void* w_v, int tokens, int heads, float* out,

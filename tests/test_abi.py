@@ -23,7 +23,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"mla_get_split_plan", "mla_decode_fwd", "mla_plan_bytes", "mla_workspace_bytes", "mla_absorb_query",
-            "mla_decompress_output"} <= set(names)
+            "mla_decompress_output", "mla_hybrid_merge"} <= set(names)
     L = ctypes.CDLL(mla.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -112,4 +112,28 @@ def test_projections_reject_bad_arguments_before_launch():
     assert L.mla_decompress_output(fake, None, 4, 16, fake, None) == 1
     assert L.mla_decompress_output(fake, fake, -1, 16, fake, None) == 1
     assert L.mla_decompress_output(fake, fake, 4, 16, fake + 4, None) == 1
+    assert b"16-byte aligned" in L.mla_last_error_message()
+
+
+def test_hybrid_merge_rejects_bad_arguments_before_launch():
+    """Status codes for the split latent + decompressed merge, returned before anything is
+    enqueued (fake, never dereferenced device addresses; no GPU needed)."""
+    L = mla.lib()
+    f = 1 << 20
+
+    def call(q_nope=f, k_new=f, n=64, out_old=f, batch=2, s_q=4, heads=16, scale=0.1, causal=0, out=f):
+        return L.mla_hybrid_merge(q_nope, f, k_new, f, f, n, out_old, f, batch, s_q, heads, scale, causal, out, f,
+                                  None)
+
+    assert call(q_nope=None) == 1                       # null pointer
+    assert call(k_new=None) == 1                        # new tokens required when n > 0
+    assert call(n=-1) == 1
+    assert call(batch=0) == 1 and call(heads=0) == 1 and call(s_q=0) == 1
+    assert call(scale=0.0) == 1 and call(scale=float("inf")) == 1
+    assert call(causal=2) == 1
+    assert call(s_q=33) == 2                            # one 32-row tile of query rows
+    assert call(batch=65536) == 2
+    assert call(n=3, s_q=4, causal=1) == 2              # causal needs n >= s_q
+    assert b"n_new >= s_q" in L.mla_last_error_message()
+    assert call(out=f + 4) == 1
     assert b"16-byte aligned" in L.mla_last_error_message()
