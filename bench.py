@@ -122,6 +122,103 @@ def projections(w, steps: int, warmup: int, copies: int = 16):
     return res
 
 
+def hybrid(steps: int, warmup: int, b: int = 32, s_q: int = 16, heads: int = 128, t: int = 4096, n: int = 640):
+    """The split latent + decompressed variant at the pages' s=16 configuration (b=32, h=128,
+    t=4096): o = t - n old tokens as a paged latent cache, the n newest decompressed (K, V of
+    128 channels per head, the shared rope key). One hybrid step = query absorption, plan and
+    latent decode over the old tokens, output decompression, then mla_hybrid_merge over the
+    new tokens (causal). Beside it the all-latent step at the same shape (absorption, plan,
+    causal decode over t tokens, decompression). n = 640 is where the cost model balances the
+    MFMA time of the latent tokens against the HBM time of the decompressed ones on MI355X.
+    Seeded random inputs generated on the device; two copies of every cache are cycled."""
+    import numpy as np
+    import torch
+    import mla_latent_space_amd as mla
+    dev = "cuda"
+    o = t - n
+    gen = torch.Generator(device=dev).manual_seed(11)
+    bf = lambda *shape: torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    scale = (128 + 64) ** -0.5
+
+    def paged(tokens, copies=2):
+        per = (tokens + 63) // 64
+        caches = [bf(b * per, 64, 576) for _ in range(copies)]
+        bt = torch.randperm(b * per, generator=gen, device=dev).to(torch.int32).view(b, per).contiguous()
+        return caches, bt, torch.full((b,), tokens, dtype=torch.int32, device=dev)
+
+    kv_old, bt_old, sl_old = paged(o)
+    kv_all, bt_all, sl_all = paged(t)
+    q_nope, q_rope = bf(b, s_q, heads, 128), bf(b, s_q, heads, 64)
+    w_k = bf(heads, 512, 128) * (128 ** -0.5)
+    w_v = bf(heads, 128, 512) * (512 ** -0.5)
+    news = [(bf(b, n, heads, 128), bf(b, n, 64), bf(b, n, heads, 128)) for _ in range(2)]
+    W = mla.default_num_workers(0)
+    qz = torch.empty((b, s_q, heads, 576), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty((b, s_q, heads, 512), dtype=torch.float32, device=dev)
+    lse_a = torch.empty((b, s_q, heads), dtype=torch.float32, device=dev)
+    out_old = torch.empty((b, s_q, heads, 128), dtype=torch.float32, device=dev)
+    out = torch.empty_like(out_old)
+    lse = torch.empty_like(lse_a)
+    ws = torch.empty(max(mla.workspace_bytes(b, s_q, heads, W), 16), dtype=torch.uint8, device=dev)
+    plan_buf = torch.empty(mla.plan_bytes(b, s_q, heads, W), dtype=torch.uint8, device=dev)
+
+    def latent_part(i, kv, bt, sl, causal):
+        mla.absorb_query(q_nope, q_rope, w_k, out=qz)
+        plan = mla.get_split_plan(sl, s_q, heads, causal, W, out=plan_buf)
+        mla.decode_fwd(qz, kv[i % 2], bt, sl, scale, causal=causal, plan=plan, workspace=ws, out=o_lat, lse=lse_a)
+        mla.decompress_output(o_lat, w_v, out=out_old)
+
+    def merge(i):
+        k_new, kr_new, v_new = news[i % 2]
+        mla.hybrid_merge(q_nope, q_rope, k_new, kr_new, v_new, out_old, lse_a, scale, causal=True, out=out, lse=lse)
+
+    def hybrid_step(i):
+        latent_part(i, kv_old, bt_old, sl_old, False)
+        merge(i)
+
+    def latent_step(i):
+        latent_part(i, kv_all, bt_all, sl_all, True)
+
+    def wall_us(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
+    hyb_us, lat_us = wall_us(hybrid_step), wall_us(latent_step)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        latent_part(i, kv_old, bt_old, sl_old, False)
+        ev[i][0].record(stream)
+        merge(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    merge_us = float(np.mean([a.elapsed_time(c) * 1e3 for a, c in ev]))
+    rows = b * s_q * heads
+    merge_bytes = b * n * heads * 128 * 2 * 2 + b * n * 64 * 2 + rows * ((128 + 64) * 2 + 2 * 128 * 4 + 2 * 4)
+    merge_flops = 4.0 * b * heads * s_q * n * 128 + 2.0 * b * heads * s_q * n * 64
+    gbps = merge_bytes / (merge_us * 1e-6) / 1e9
+    # the pages' cost models (FLOPs, bytes at w = 2)
+    lat_flops = 2.0 * b * heads * s_q * t * (2 * K_LAT + P_ROPE)
+    lat_bytes = 2.0 * (b * heads * s_q * (2 * K_LAT + P_ROPE) + b * t * (K_LAT + P_ROPE))
+    hyb_flops = 2.0 * b * heads * s_q * t * P_ROPE + 4.0 * b * heads * s_q * n * 128 + 4.0 * b * heads * s_q * o * K_LAT
+    hyb_bytes = 2.0 * (b * heads * s_q * (P_ROPE + 128 + K_LAT) + b * o * K_LAT + b * t * P_ROPE
+                       + 2 * b * heads * n * 128 + b * heads * s_q * (128 + K_LAT))
+    bound = lambda f, by: max(f / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBPS * 1e9)) * 1e6
+    return {"workload": f"b={b} s={s_q} h={heads} t={t}: o={o} latent (bf16 paged) + n={n} decompressed, causal",
+            "hybrid_step_us": round(hyb_us, 2), "latent_step_us": round(lat_us, 2),
+            "merge_us": round(merge_us, 2),
+            "merge_roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                               "frac": round(gbps / PEAK_HBM_GBPS, 4), "bytes": merge_bytes, "flops": merge_flops},
+            "cost_model_bound_us": {"latent": round(bound(lat_flops, lat_bytes), 1),
+                                    "hybrid": round(bound(hyb_flops, hyb_bytes), 1)}}
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle (as is) over the workload's sequences, one at a time, until ~budget_s of
     host time (whole passes over the batch are repeated if one pass is shorter), scaled to
@@ -162,6 +259,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-projections", action="store_true",
                     help="skip timing the query-absorption and output-decompression kernels")
+    ap.add_argument("--no-hybrid", action="store_true",
+                    help="skip the split latent + decompressed variant's leg")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times (the reference "
                          "kernel for scaling HBM byte counters), print its size and exit")
@@ -285,6 +384,8 @@ def main():
     }
     if w.kv_dtype == "bf16" and not args.no_projections:
         rec["projections"] = projections(w, args.steps, min(args.warmup, 50))
+    if w.kv_dtype == "bf16" and not args.no_hybrid:
+        rec["hybrid"] = hybrid(min(args.steps, 50), min(args.warmup, 20))
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)
