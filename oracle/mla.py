@@ -15,6 +15,10 @@ Definitions followed (page "Mla Analysis", skillmd.com):
 * Section "MLAvar6+ Design": o old tokens as latent rows, n new tokens decompressed,
   t = o + n; the attention over their union is exact.
 
+Library card page "FlashMLA: Efficient Multi-head Latent Attention Kernels", its
+description and use cases: token-level sparse attention for decoding, with an FP8 cache
+(decode_sparse).
+
 FlashMLA-2 newsletter page, section "Architectural Analysis": the latent cache may be
 stored in FP8 and scaled up before the matrix products; OCP e4m3fn is the format read
 here, one float32 scale per token per 128-channel tile.
@@ -155,6 +159,36 @@ def decode_latent_rows(q_bits, kv, kv_scales, kv_dtype, block_table, seqlens, sc
         o, l = softmax_attention(qz, z[:vis], z[:vis, :K_LAT], scale)
         out[n] = o[0]
         lse[n] = l[0]
+    return out, lse
+
+
+def sparse_keys(indices_row: np.ndarray, t: int) -> np.ndarray:
+    """Library card page "FlashMLA: Efficient Multi-head Latent Attention Kernels" (token-level
+    sparse attention in decoding): a query token attends to its own list of selected tokens
+    instead of the whole cache. Reading: the list holds logical positions of the query's sequence; an entry outside
+    [0, t) is padding and dropped; the others are keys in list order (a repeated position is a
+    repeated key). Returns the kept positions."""
+    idx = np.asarray(indices_row, dtype=np.int64)
+    return idx[(idx >= 0) & (idx < t)]
+
+
+def decode_sparse(q_bits: np.ndarray, kv: np.ndarray, kv_scales: Optional[np.ndarray], kv_dtype: str,
+                  block_table: np.ndarray, seqlens: np.ndarray, indices: np.ndarray, scale: float,
+                  seqs: Optional[Iterable[int]] = None):
+    """Token-level sparse latent decode: query (i, j) attends over the latent rows at
+    sparse_keys(indices[i, j], t_i), with the same scores, softmax and value as the dense decode.
+    q_bits [b, s, h, 576] bf16 bits, indices int [b, s, topk]; returns out [b, s, h, 512] and
+    lse [b, s, h] (rows of sequences not in ``seqs`` are left NaN)."""
+    b, s_q, h, _ = q_bits.shape
+    out = np.full((b, s_q, h, K_LAT), np.nan)
+    lse = np.full((b, s_q, h), np.nan)
+    for i in (range(b) if seqs is None else seqs):
+        t = int(seqlens[i])
+        z = latent_rows(kv, kv_scales, kv_dtype, block_table[i], t)
+        for j in range(s_q):
+            keys = z[sparse_keys(indices[i, j], t)]
+            qz = bf16_bits_to_f64(q_bits[i, j])
+            out[i, j], lse[i, j] = softmax_attention(qz, keys, keys[:, :K_LAT], scale)
     return out, lse
 
 
