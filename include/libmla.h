@@ -181,6 +181,51 @@ int32_t mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_k
 int32_t mla_decompress_output(const float* out_latent, const void* w_v, int32_t tokens, int32_t heads,
                               float* out, void* stream);
 
+/* Token-level sparse decode (library card page "FlashMLA: Efficient Multi-head Latent Attention
+ * Kernels": sparse attention over selected tokens in decoding, with an FP8 cache). Each query
+ * token (sequence i, token j) attends to its own list indices[i, j, 0:topk] of logical token
+ * positions of sequence i instead of all its cached tokens: an entry u with
+ * 0 <= u < min(t_i, max_pages * 64) is a key (the latent row at block_table[i, u / 64], slot
+ * u % 64; a listed position twice is two keys), any other entry is padding. The formulas of the
+ * header comment apply with these keys as the visible set (no causal mask: the list is the
+ * visible set); an empty list gives out = 0, lse = -inf. Two calls: mla_get_sparse_plan turns
+ * the lists into cache-row lists and a split plan over the batch * s_q query tokens (each one a
+ * sequence of one query row per head), mla_sparse_decode_fwd runs the decode. */
+
+/* Bytes of the row-list buffer of mla_get_sparse_plan (batch * s_q lists of topk rounded up to
+ * 32 entries, then batch * s_q counts), or 0 for an invalid shape. */
+size_t mla_sparse_rows_bytes(int32_t batch, int32_t s_q, int32_t topk);
+
+/* indices     device int32 [batch, s_q, topk].
+ * topk        1 .. 2^20 entries per query token.
+ * block_table, max_pages, seqlens, num_pages   as for mla_decode_fwd (the same preconditions).
+ * batch, s_q  batch >= 1, s_q 1 .. 64, batch * s_q <= 16384.
+ * heads       128 (one 128-row tile per query token).
+ * num_pages   pages of the cache; num_pages * 64 * 640 must be below 2^31 (31-bit row offsets).
+ * num_workers 1 .. 4096.
+ * rows        device buffer of >= mla_sparse_rows_bytes(batch, s_q, topk) bytes, 16-byte aligned;
+ *             written by the device; opaque; valid for mla_sparse_decode_fwd calls with the same
+ *             indices, block table and lengths.
+ * plan        device buffer of >= mla_plan_bytes(batch * s_q, 1, 128, num_workers) bytes, 16-byte
+ *             aligned; written by the device.
+ * Runs entirely on the device. Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
+ * MLA_ERR_WORKSPACE_TOO_SMALL (rows_bytes or plan_bytes), MLA_ERR_HIP. */
+int32_t mla_get_sparse_plan(const int32_t* indices, int32_t topk, const int32_t* block_table, int32_t max_pages,
+                            const int32_t* seqlens, int32_t batch, int32_t s_q, int32_t heads, int64_t num_pages,
+                            int32_t num_workers, void* rows, size_t rows_bytes, void* plan, size_t plan_bytes,
+                            void* stream);
+
+/* q, out, lse as for mla_decode_fwd ([batch, s_q, 128, ...]). kv_cache, kv_scales: the fp8 cache
+ * (kv_dtype must be MLA_KV_FP8_E4M3; a bf16 cache is MLA_ERR_UNSUPPORTED here). rows, plan: from
+ * mla_get_sparse_plan with the same batch, s_q, heads, topk, num_pages and num_workers.
+ * workspace: >= mla_workspace_bytes(batch * s_q, 1, 128, num_workers) bytes (or NULL when that is
+ * 0), 16-byte aligned. Results for a fixed plan are bitwise reproducible.
+ * Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP. */
+int32_t mla_sparse_decode_fwd(const void* q, const void* kv_cache, const float* kv_scales, int32_t kv_dtype,
+                              int64_t num_pages, int32_t batch, int32_t s_q, int32_t heads, int32_t topk,
+                              float softmax_scale, const void* rows, const void* plan, int32_t num_workers,
+                              void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream);
+
 /* Split latent + decompressed attention (page "Mla Analysis", section "MLAvar6+ Design"): a
  * sequence's t cached tokens are split into o old tokens kept as latent rows and its n newest
  * kept decompressed (per head K and V of 128 channels, with the shared 64-channel rope key).

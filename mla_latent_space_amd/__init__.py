@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["MlaError", "SplitPlan", "lib", "abi_version", "default_num_workers", "plan_bytes", "workspace_bytes",
            "absorb_query", "decompress_output",
-           "get_split_plan", "decode_fwd", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3", "hybrid_merge"]
+           "get_split_plan", "decode_fwd", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3", "hybrid_merge", "SparsePlan", "get_sparse_plan", "sparse_decode_fwd"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 KV_BF16 = 0
@@ -66,6 +66,14 @@ def lib() -> ctypes.CDLL:
     L.mla_absorb_query.argtypes = [c_p, c_p, c_p, c_i32, c_i32, c_p, c_p]
     L.mla_decompress_output.restype = c_i32
     L.mla_decompress_output.argtypes = [c_p, c_p, c_i32, c_i32, c_p, c_p]
+    L.mla_sparse_rows_bytes.restype = c_sz
+    L.mla_sparse_rows_bytes.argtypes = [c_i32, c_i32, c_i32]
+    L.mla_get_sparse_plan.restype = c_i32
+    L.mla_get_sparse_plan.argtypes = [c_p, c_i32, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i64, c_i32, c_p, c_sz,
+                                      c_p, c_sz, c_p]
+    L.mla_sparse_decode_fwd.restype = c_i32
+    L.mla_sparse_decode_fwd.argtypes = [c_p, c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_f, c_p, c_p,
+                                        c_i32, c_p, c_sz, c_p, c_p, c_p]
     L.mla_hybrid_merge.restype = c_i32
     L.mla_hybrid_merge.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_f, c_i32, c_p,
                                    c_p, c_p]
@@ -253,4 +261,63 @@ def hybrid_merge(q_nope: torch.Tensor, q_rope: torch.Tensor, k_new: Optional[tor
     _check(int(lib().mla_hybrid_merge(q_nope.data_ptr(), q_rope.data_ptr(), ptr(k_new), ptr(kr_new), ptr(v_new), n,
                                       out_old.data_ptr(), lse_old.data_ptr(), b, s_q, heads, float(softmax_scale),
                                       1 if causal else 0, out.data_ptr(), lse.data_ptr(), _stream(q_nope))))
+    return out, lse
+
+
+class SparsePlan:
+    """Cache-row lists and split plan of a token-sparse decode (see mla_get_sparse_plan)."""
+
+    def __init__(self, rows, plan, batch, s_q, heads, topk, num_pages, num_workers):
+        self.rows, self.plan = rows, plan
+        self.batch, self.s_q, self.heads, self.topk = batch, s_q, heads, topk
+        self.num_pages, self.num_workers = num_pages, num_workers
+
+
+def get_sparse_plan(indices: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor, num_pages: int,
+                    heads: int = 128, num_workers: Optional[int] = None) -> SparsePlan:
+    """indices int32 [b, s, topk] (logical token positions; entries outside [0, t) are padding),
+    block_table int32 [b, max_pages], seqlens int32 [b]."""
+    if indices.dim() != 3 or indices.dtype != torch.int32 or not indices.is_cuda or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous CUDA int32 tensor [batch, s_q, topk]")
+    b, s_q, topk = (int(x) for x in indices.shape)
+    for name, t in (("block_table", block_table), ("seqlens", seqlens)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA int32 tensor")
+    W = default_num_workers(indices.device.index or 0) if num_workers is None else int(num_workers)
+    rb = int(lib().mla_sparse_rows_bytes(b, s_q, topk))
+    pb = plan_bytes(b * s_q, 1, heads, W)
+    if rb == 0 or pb == 0:
+        raise MlaError(2, f"unsupported sparse shape b={b} s_q={s_q} topk={topk} heads={heads}")
+    rows = torch.empty(rb, dtype=torch.uint8, device=indices.device)
+    plan = torch.empty(pb, dtype=torch.uint8, device=indices.device)
+    _check(int(lib().mla_get_sparse_plan(indices.data_ptr(), topk, block_table.data_ptr(), int(block_table.shape[1]),
+                                         seqlens.data_ptr(), b, s_q, heads, int(num_pages), W, rows.data_ptr(), rb,
+                                         plan.data_ptr(), pb, _stream(indices))))
+    return SparsePlan(rows, plan, b, s_q, heads, topk, int(num_pages), W)
+
+
+def sparse_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, kv_scales: torch.Tensor, softmax_scale: float,
+                      plan: SparsePlan, workspace: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Token-sparse decode over an fp8 cache (see mla_sparse_decode_fwd). q bf16 [b, s, 128, 576];
+    kv_cache uint8 [pages, 64, 640]; kv_scales float32 [pages, 64, 4]. Returns out float32
+    [b, s, 128, 512] and lse float32 [b, s, 128]."""
+    b, s_q, heads = plan.batch, plan.s_q, plan.heads
+    _need(q, "q", torch.bfloat16, (b, s_q, heads, 576))
+    if kv_cache.dtype not in (torch.uint8, torch.float8_e4m3fn) or int(kv_cache.shape[0]) != plan.num_pages:
+        raise ValueError("kv_cache must be the fp8 layout [num_pages, 64, 640] the plan was built for")
+    W = plan.num_workers
+    need = workspace_bytes(b * s_q, 1, heads, W)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(b, s_q, heads, 512, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(b, s_q, heads, dtype=torch.float32, device=q.device)
+    _check(int(lib().mla_sparse_decode_fwd(
+        q.data_ptr(), kv_cache.data_ptr(), kv_scales.data_ptr(), KV_FP8_E4M3, plan.num_pages, b, s_q, heads, plan.topk,
+        float(softmax_scale), plan.rows.data_ptr(), plan.plan.data_ptr(), W,
+        None if workspace is None else workspace.data_ptr(),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), out.data_ptr(), lse.data_ptr(),
+        _stream(q))))
     return out, lse

@@ -1,5 +1,6 @@
 // libmla C ABI: host-side validation, sizing and dispatch. Every check here happens before
 // any work is enqueued; the library allocates nothing and keeps no pointer across calls.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -203,6 +204,109 @@ int32_t mla_decompress_output(const float* out_latent, const void* w_v, int32_t 
     return fail(MLA_ERR_INVALID_ARG, "out_latent, w_v and out must be 16-byte aligned");
   hipError_t e = mla::launch_decompress_output(out_latent, w_v, tokens, heads, out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decompression kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t mla_sparse_rows_bytes(int32_t batch, int32_t s_q, int32_t topk) {
+  if (batch < 1 || s_q < 1 || topk < 1 || topk > mla::kSparseMaxTopk || (int64_t)batch * s_q > mla::kMaxItems)
+    return 0;
+  const int64_t n = (int64_t)batch * s_q;
+  return (size_t)((n * mla::sparse_stride(topk) + n) * 4 + 15) / 16 * 16;
+}
+
+// Shape checks of the token-sparse calls; the plan and decode shapes are those of batch * s_q
+// sequences of one query token.
+static int32_t check_sparse(int32_t batch, int32_t s_q, int32_t heads, int32_t topk, int64_t num_pages,
+                            int32_t num_workers) {
+  if (batch < 1 || s_q < 1) return fail(MLA_ERR_INVALID_ARG, "batch and s_q must be >= 1 (got %d, %d)", batch, s_q);
+  if (topk < 1) return fail(MLA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", topk);
+  if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1 (got %lld)", (long long)num_pages);
+  if (heads != mla::kSparseHeads)
+    return fail(MLA_ERR_UNSUPPORTED, "the token-sparse decode needs heads = %d (got %d)", mla::kSparseHeads, heads);
+  if (topk > mla::kSparseMaxTopk) return fail(MLA_ERR_UNSUPPORTED, "topk must be <= %d", mla::kSparseMaxTopk);
+  if (s_q > 64) return fail(MLA_ERR_UNSUPPORTED, "s_q must be <= 64 (got %d)", s_q);
+  if (num_pages * mla::kPage * (mla::kLat + 2 * mla::kRope) >= (1LL << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "the token-sparse decode addresses the cache with 31-bit offsets: num_pages "
+                "must be below %lld", (long long)((1LL << 31) / (mla::kPage * (mla::kLat + 2 * mla::kRope))));
+  return check_shape((int32_t)std::min<int64_t>((int64_t)batch * s_q, 1LL << 30), 1, heads, 0, num_workers);
+}
+
+int32_t mla_get_sparse_plan(const int32_t* indices, int32_t topk, const int32_t* block_table, int32_t max_pages,
+                            const int32_t* seqlens, int32_t batch, int32_t s_q, int32_t heads, int64_t num_pages,
+                            int32_t num_workers, void* rows, size_t rows_bytes, void* plan, size_t plan_bytes,
+                            void* stream) {
+  int32_t st = check_sparse(batch, s_q, heads, topk, num_pages, num_workers);
+  if (st != MLA_OK) return st;
+  if (!indices || !block_table || !seqlens || !rows || !plan)
+    return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL (indices, block_table, seqlens, rows, plan)");
+  if (max_pages < 1 || max_pages > mla::kMaxPagesPerSeq)
+    return fail(max_pages < 1 ? MLA_ERR_INVALID_ARG : MLA_ERR_UNSUPPORTED, "max_pages must be in 1..%d (got %d)",
+                mla::kMaxPagesPerSeq, max_pages);
+  if (!aligned16(rows) || !aligned16(plan)) return fail(MLA_ERR_INVALID_ARG, "rows and plan must be 16-byte aligned");
+  const int32_t n = batch * s_q;
+  const size_t need_rows = mla_sparse_rows_bytes(batch, s_q, topk);
+  if (rows_bytes < need_rows)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "rows_bytes %zu < required %zu", rows_bytes, need_rows);
+  const size_t need_plan = plan_bytes_of(n, 1, heads, num_workers);
+  if (plan_bytes < need_plan)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "plan_bytes %zu < required %zu", plan_bytes, need_plan);
+  const int stride = mla::sparse_stride(topk);
+  int32_t* rows32 = static_cast<int32_t*>(rows);
+  int32_t* vis = rows32 + (int64_t)n * stride;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_sparse_rows(indices, topk, block_table, max_pages, seqlens, batch, s_q, num_pages,
+                                         rows32, stride, vis, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "row-list kernel launch: %s", hipGetErrorString(e));
+  e = mla::launch_plan(vis, n, 1, heads, 0, num_workers, static_cast<int32_t*>(plan), s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t mla_sparse_decode_fwd(const void* q, const void* kv_cache, const float* kv_scales, int32_t kv_dtype,
+                              int64_t num_pages, int32_t batch, int32_t s_q, int32_t heads, int32_t topk,
+                              float softmax_scale, const void* rows, const void* plan, int32_t num_workers,
+                              void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream) {
+  int32_t st = check_sparse(batch, s_q, heads, topk, num_pages, num_workers);
+  if (st != MLA_OK) return st;
+  if (!q || !kv_cache || !kv_scales || !rows || !plan || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL (q, kv_cache, kv_scales, rows, plan, out, lse)");
+  if (kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(kv_dtype == MLA_KV_BF16 ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG,
+                "the token-sparse decode reads an fp8 e4m3 cache (kv_dtype %d)", kv_dtype);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(kv_scales) || !aligned16(out) || !aligned16(plan) ||
+      !aligned16(rows) || (workspace && !aligned16(workspace)))
+    return fail(MLA_ERR_INVALID_ARG, "q, kv_cache, kv_scales, rows, out, plan and workspace must be 16-byte aligned");
+  const int32_t n = batch * s_q;
+  const size_t need = workspace_bytes_of(n, 1, heads, num_workers);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace ? workspace_bytes : 0,
+                need);
+  const int stride = mla::sparse_stride(topk);
+  mla::DecodeArgs a;
+  a.q = q;
+  a.kv = kv_cache;
+  a.kv_scales = kv_scales;
+  a.num_pages = num_pages;
+  a.block_table = nullptr;
+  a.max_pages = (stride + mla::kPage - 1) / mla::kPage;   // caps no list: vis <= topk <= stride
+  a.seqlens = static_cast<const int32_t*>(rows) + (int64_t)n * stride;
+  a.batch = n;
+  a.s_q = 1;
+  a.heads = heads;
+  a.causal = 0;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.plan = static_cast<const int32_t*>(plan);
+  a.workers = num_workers;
+  a.ws = static_cast<float*>(workspace);
+  a.out = out;
+  a.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_decode_sparse_fp8(a, static_cast<const int32_t*>(rows), stride, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
+  e = mla::launch_combine_rows32(a, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
 

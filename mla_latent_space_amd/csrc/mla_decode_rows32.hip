@@ -68,6 +68,11 @@ constexpr int kR8QBase = kR8PBase + 2 * kR32PBytes;         // Q^T k-steps 34, 3
 constexpr int kR8LdsTotal = kR8QBase + 4 * 2048;
 static_assert(kR8LdsTotal <= 160 * 1024, "LDS budget (fp8)");
 static_assert(kR8LdsTotal >= kR32Slots * kBufBytes, "the query rows are staged through LDS at start-up");
+// token-sparse fp8: a ring of 4 x 32 cache-row numbers (one per step; 256 B per slot) in the
+// last KiB
+constexpr int kR8RowRing = kR8LdsTotal;
+constexpr int kR8SparseLdsTotal = kR8RowRing + 4 * 256;
+static_assert(kR8SparseLdsTotal <= 160 * 1024, "LDS budget (token-sparse fp8)");
 static_assert(kR8StBase % 128 == 0 && kR8StBytes % 128 == 0 && kBufBytes % 128 == 0,
               "slot offsets leave the low 7 address bits to the lane's swizzle");
 constexpr float kWindow = 64.f;                  // rows may exceed their reference max by 2^64
@@ -140,10 +145,11 @@ __device__ __forceinline__ bf16x4 dequant4(uint32_t w, float sc) {
   r[3] = (__bf16)(hi[1] * sc);
   return r;
 }
-// s_waitcnt for the fp8 DMA steps: wave 0 issues 6 instructions per step, the others 5
-template <int kSteps>
+// s_waitcnt for the fp8 DMA steps: wave 0 issues 6 instructions per step (the scales), wave 1
+// 6 on a token-sparse cache (the next row numbers), the others 5
+template <int kSteps, bool kSparse>
 __device__ __forceinline__ void wait_f8_steps(int wave) {
-  if (wave == 0) wait_vmcnt<6 * kSteps>();
+  if (wave == 0 || (kSparse && wave == 1)) wait_vmcnt<6 * kSteps>();
   else wait_vmcnt<5 * kSteps>();
 }
 
@@ -231,11 +237,13 @@ __device__ __forceinline__ PvAddr pv_at(const PvAddr& base, uint32_t zoff) {
   return r;
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kSparse>
 __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     const __bf16* __restrict__ q_ptr, const char* __restrict__ kv_ptr, const float* __restrict__ kv_scales,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ plan, float* __restrict__ ws,
-    float* __restrict__ out_ptr, float* __restrict__ lse_ptr, Scalars a) {
+    float* __restrict__ out_ptr, float* __restrict__ lse_ptr, const int32_t* __restrict__ srows, int srow_stride,
+    Scalars a) {
+  static_assert(kFp8 || !kSparse, "the token-sparse path reads an fp8 cache");
   constexpr int kPBase = kFp8 ? kR8PBase : kR32PBase;   // P buffers; votes and 1/l after the loop
   constexpr int kLoadSlots = kFp8 ? kR8Stage : kR32Slots;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
@@ -284,33 +292,68 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   // ---- load cursor: the first kR32Slots-1 steps are issued up front, then one step per
   // compute region (its DMA instructions spread between the score MFMAs)
   LoadCursor lc;
-  cursor_enter(lc, plan, kb, kb, pb, ke, pe);
-  auto settle = [&]() {
-    while (lc.k <= k_last && lc.hh >= lc.hh1) {
-      if (lc.k == k_last) {
-        lc.k = k_last + 1;
+  auto settle_c = [&](LoadCursor& c) {
+    while (c.k <= k_last && c.hh >= c.hh1) {
+      if (c.k == k_last) {
+        c.k = k_last + 1;
         break;
       }
-      cursor_enter(lc, plan, lc.k + 1, kb, pb, ke, pe);
+      cursor_enter(c, plan, c.k + 1, kb, pb, ke, pe);
     }
   };
-  settle();
-  if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
+  auto restart = [&](LoadCursor& c, int k) {
+    cursor_enter(c, plan, k, kb, pb, ke, pe);
+    settle_c(c);
+    if (!kSparse && c.k <= k_last) cursor_fetch(c, a, block_table);
+  };
+  restart(lc, kb);
   int load_slot = 0;   // ring slot (bf16) or staging slot (fp8) of the cursor's step
+  // token-sparse: a second cursor two steps ahead loads each step's 32 cache-row numbers
+  // (stored + 1; 0 = none) into the row ring; row_slot is the ring slot of lc's step
+  LoadCursor pc;
+  int row_slot = 0;
+  if constexpr (kSparse) restart(pc, kb);
   auto advance = [&]() {
     load_slot = load_slot + 1 == kLoadSlots ? 0 : load_slot + 1;
     ++lc.hh;
-    settle();
-    if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
+    settle_c(lc);
+    if (!kSparse && lc.k <= k_last) cursor_fetch(lc, a, block_table);
+    if constexpr (kSparse) row_slot = (row_slot + 1) & 3;
+  };
+  auto advance_pc = [&]() {
+    ++pc.hh;
+    settle_c(pc);
   };
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
   const DmaOffsets dmo = dma_offsets(wave, lane);   // this wave's DMA source offsets
   // descriptors of the cursor's step (zero-record loads past the worker's range)
   auto step_rsrc = [&]() -> StepRsrc {
-    if (lc.k <= k_last) return cursor_rsrc<kFp8>(lc, a, kv_ptr, kv_scales);
     StepRsrc z;
+    if (lc.k <= k_last) {
+      if constexpr (kSparse) {   // the whole cache (its size is checked below 2^31 on the host)
+        z.kv = make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), (int)(a.num_pages * (kPage * kF8Row)));
+        z.sc = make_rsrc(reinterpret_cast<uint64_t>(kv_scales), (int)(a.num_pages * (kPage * 16)));
+        return z;
+      } else {
+        return cursor_rsrc<kFp8>(lc, a, kv_ptr, kv_scales);
+      }
+    }
     z.kv = z.sc = make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
     return z;
+  };
+  // token-sparse: the row numbers of pc's step into row ring slot rs_slot (wave 1; lanes 32..63
+  // read on into the slot's second half or past the list, harmlessly)
+  auto dma_rows = [&](int rs_slot) {
+    if constexpr (kSparse) {
+      if (wave == 1) {
+        const i32x4 r = pc.k <= k_last ? make_rsrc(reinterpret_cast<uint64_t>(srows) +
+                                                        (uint64_t)pc.seq * (uint64_t)srow_stride * 4u,
+                                                    srow_stride * 4)
+                                       : make_rsrc(reinterpret_cast<uint64_t>(srows), 0);
+        lds_dma_x1(lds_u32 + kR8RowRing + 256u * (uint32_t)rs_slot, 4u * (32u * (uint32_t)pc.hh + (uint32_t)lane), r);
+      }
+      advance_pc();
+    }
   };
   // fp8: this lane's DMA source offsets and its addresses for dequantising (token
   // 16 half + l/4, channels 128 wave + 32c + 8(l%4) .. +7 of piece c: the staging read, where
@@ -321,21 +364,42 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   if constexpr (kFp8) {
     const uint32_t l = (uint32_t)lane, u = l >> 2, sub = l & 3u, ur = 8u * (uint32_t)wave + (l >> 3);
     const F8Dma d = f8_dma_offsets(wave, lane);
-    f8_dma = d.codes | (d.rope << 16);
+    // (token-sparse: the offsets within the lane's row; the row comes from the row ring)
+    const uint32_t u0 = 2u * (uint32_t)wave + (l >> 5);
+    f8_dma = kSparse ? (d.codes - u0 * kF8Row) | ((d.rope - ur * kF8Row) << 16) : d.codes | (d.rope << 16);
     f8_dq = (u * kLat + ((128u * (uint32_t)wave + 8u * sub) ^ (32u * (u & 7u)))) |
             ((u * kRowBytes + 256u * (uint32_t)wave + 16u * (sub ^ sw32(u))) << 16);
     f8_aux = (kR8StScales + 16u * u + 4u * (uint32_t)wave) | ((ur * kRowBytes + 16u * (64u + ((l & 7u) ^ sw32(ur)))) << 16);
     static_assert(kR8StBytes < 65536 && 16 * kRowBytes < 65536 && kBufBytes < 65536, "16-bit offsets");
   }
+  // token-sparse: the stored row number (+1; 0 = none) of the token this lane loads with fp8
+  // instruction j of lc's step (codes: token 8j + 2 wave + l/32; rope: 8 wave + l/8; scales: l)
+  auto f8_row = [&](int j) -> uint32_t {
+    const uint32_t tok = j < 4 ? 8u * (uint32_t)j + 2u * (uint32_t)wave + ((uint32_t)lane >> 5)
+                               : (j == 4 ? 8u * (uint32_t)wave + ((uint32_t)lane >> 3) : ((uint32_t)lane & 31u));
+    return *(const uint32_t __attribute__((address_space(3)))*)(lds + (kR8RowRing + 256u * (uint32_t)row_slot + 4u * tok));
+  };
   // one step's DMA instructions into staging slot st (LDS address); fp8 instruction j of
-  // this wave (0..3 codes, 4 rope, 5 scales on wave 0)
-  auto dma_f8 = [&](const StepRsrc& rs, uint32_t st, int j) {
-    if (j < 4) {
-      lds_dma_x4(st + 1024u * (uint32_t)(wave + 4 * j), (f8_dma & 0xFFFFu) + 8u * kF8Row * (uint32_t)j, rs.kv);
-    } else if (j == 4) {
-      lds_dma_x4(st + kR8StRope + 1024u * (uint32_t)wave, f8_dma >> 16, rs.kv);
-    } else if (wave == 0) {
-      lds_dma_x4(st + kR8StScales, lane < 32 ? 16u * (uint32_t)lane : 0x40000000u, rs.sc);
+  // this wave (0..3 codes, 4 rope, 5 scales on wave 0); sv: f8_row(j) on a token-sparse
+  // cache (a row of none reads past the range: zeros)
+  auto dma_f8 = [&](const StepRsrc& rs, uint32_t st, int j, uint32_t sv) {
+    if constexpr (kSparse) {
+      const uint32_t none = 0xFFFFFFF0u;
+      if (j < 4) {
+        lds_dma_x4(st + 1024u * (uint32_t)(wave + 4 * j), sv ? (sv - 1u) * kF8Row + (f8_dma & 0xFFFFu) : none, rs.kv);
+      } else if (j == 4) {
+        lds_dma_x4(st + kR8StRope + 1024u * (uint32_t)wave, sv ? (sv - 1u) * kF8Row + (f8_dma >> 16) : none, rs.kv);
+      } else if (wave == 0) {
+        lds_dma_x4(st + kR8StScales, (sv && lane < 32) ? (sv - 1u) * 16u : none, rs.sc);
+      }
+    } else {
+      if (j < 4) {
+        lds_dma_x4(st + 1024u * (uint32_t)(wave + 4 * j), (f8_dma & 0xFFFFu) + 8u * kF8Row * (uint32_t)j, rs.kv);
+      } else if (j == 4) {
+        lds_dma_x4(st + kR8StRope + 1024u * (uint32_t)wave, f8_dma >> 16, rs.kv);
+      } else if (wave == 0) {
+        lds_dma_x4(st + kR8StScales, lane < 32 ? 16u * (uint32_t)lane : 0x40000000u, rs.sc);
+      }
     }
   };
   auto issue_step = [&]() {
@@ -343,7 +407,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     if constexpr (kFp8) {
       const uint32_t st = lds_u32 + kR8StBase + (uint32_t)load_slot * kR8StBytes;
 #pragma unroll
-      for (int j = 0; j < 6; ++j) dma_f8(rs, st, j);
+      for (int j = 0; j < 6; ++j) dma_f8(rs, st, j, kSparse ? f8_row(j) : 0u);
     } else {
 #pragma unroll
       for (int n = 0; n < kR32Dma; ++n) issue32(rs.kv, lds_u32 + load_slot * kBufBytes, n, dma_voff(dmo, n), wave);
@@ -396,19 +460,43 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   // That is the state every step region starts from: region i computes the values of step i
   // and the scores of step i+1, dequantises step i+2 (staging slot) into the bf16 slot of
   // step i, and loads step i+4.
+  // Token-sparse: first the row numbers of steps g0 .. g0+3 (row ring slots 0..3), and of
+  // g0+4, g0+5 into slots 0, 1 once the loads of g0, g0+1 have read them; afterwards row_slot
+  // is 0 (step g0+4) and region i loads the rows of step i+6 into the slot two ahead.
   auto f8_fill = [&]() {
-    issue_step();
-    issue_step();
-    issue_step();
-    wait_f8_steps<2>(wave);
-    barrier_lds();
-    f8_dequant_step(kR8StBase, 0);
-    wait_f8_steps<1>(wave);
-    barrier_lds();
-    issue_step();
-    f8_dequant_step(kR8StBase + kR8StBytes, kBufBytes);
-    wait_f8_steps<1>(wave);
-    barrier_lds();
+    if constexpr (kSparse) {
+#pragma unroll 1
+      for (int r = 0; r < 4; ++r) dma_rows(r);
+      wait_vmcnt<0>();
+      barrier_lds();
+      issue_step();
+      issue_step();
+      barrier_lds();   // every wave has read ring slots 0, 1
+      dma_rows(0);
+      dma_rows(1);
+      issue_step();
+      wait_vmcnt<0>();
+      barrier_lds();
+      f8_dequant_step(kR8StBase, 0);
+      barrier_lds();   // staging slot 0 read by every wave
+      issue_step();
+      f8_dequant_step(kR8StBase + kR8StBytes, kBufBytes);
+      wait_f8_steps<1, true>(wave);
+      barrier_lds();
+    } else {
+      issue_step();
+      issue_step();
+      issue_step();
+      wait_f8_steps<2, false>(wave);
+      barrier_lds();
+      f8_dequant_step(kR8StBase, 0);
+      wait_f8_steps<1, false>(wave);
+      barrier_lds();
+      issue_step();
+      f8_dequant_step(kR8StBase + kR8StBytes, kBufBytes);
+      wait_f8_steps<1, false>(wave);
+      barrier_lds();
+    }
   };
   // Start-up: the first item's 128 query rows (147 KB, contiguous in q) are staged through
   // the four ring slots by LDS-DMA, 32 rows per slot in the cache-step layout, and each wave
@@ -681,6 +769,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
 #pragma unroll
             for (int t = 0; t < kF8QkRing; ++t) qring[t] = qk_read(qa, t);
             bf16x8 qx[2];
+            uint32_t f8_sv = 0;
 #pragma unroll
             for (int t = 0; t < 36; ++t) {
               const bf16x8 cur = qring[t % kF8QkRing];
@@ -690,7 +779,9 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
               if (t >= 18 && t < 26 && !(t & 1)) bz0[(t - 18) >> 1] = pv_read(pa, (t - 18) >> 1);
               if (t == 0) mfma_v0(s, cur, qreg[0]);
               else mfma_v(s, cur, t >= 34 ? qx[t - 34] : qreg[t]);
-              if ((t & 3) == 3 && t < 24) dma_f8(rs, lslot, t >> 2);
+              if (kSparse && (t & 3) == 1 && t < 24) f8_sv = f8_row(t >> 2);   // (two MFMAs ahead)
+              if ((t & 3) == 3 && t < 24) dma_f8(rs, lslot, t >> 2, f8_sv);
+              if (t == 27) dma_rows((row_slot + 2) & 3);   // token-sparse: rows of step i+6
               if (t == 14) f8_piece(0, 0);
               if (t == 15) f8_piece(0, 1);
               if (t == 17) f8_piece(0, 2);
@@ -809,7 +900,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         // waits for that counter anyway
         advance();
         // everything but this region's DMA: the data of step i+2 (bf16) or i+3 (fp8)
-        if constexpr (kFp8) wait_f8_steps<1>(wave);
+        if constexpr (kFp8) wait_f8_steps<1, kSparse>(wave);
         else wait_vmcnt<kR32Dma>();
         barrier_lds();
         comp_slot = cs_next;
@@ -846,9 +937,11 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       m_seen = -INFINITY;
       l_run = 0.f;
       window_exceeded = false;
-      cursor_enter(lc, plan, k, kb, pb, ke, pe);
-      settle();
-      if (lc.k <= k_last) cursor_fetch(lc, a, block_table);
+      restart(lc, k);
+      if constexpr (kSparse) {
+        restart(pc, k);
+        row_slot = 0;
+      }
       load_slot = 0;
       comp_slot = 0;
       if constexpr (kFp8) {
@@ -1091,29 +1184,33 @@ __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32
   }
 }
 
-template <bool kFp8>
-hipError_t launch_rows32(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int lds_bytes = kFp8 ? kR8LdsTotal : kR32LdsTotal;
+template <bool kFp8, bool kSparse>
+hipError_t launch_rows32(const DecodeArgs& a, const int32_t* srows, int srow_stride, hipStream_t stream) {
+  constexpr int lds_bytes = kSparse ? kR8SparseLdsTotal : (kFp8 ? kR8LdsTotal : kR32LdsTotal);
   static thread_local int configured = -1;   // the LDS opt-in is per device
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (configured != dev) {
-    e = hipFuncSetAttribute((const void*)decode_rows32_kernel<kFp8>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            lds_bytes);
+    e = hipFuncSetAttribute((const void*)decode_rows32_kernel<kFp8, kSparse>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     configured = dev;
   }
-  hipLaunchKernelGGL(decode_rows32_kernel<kFp8>, dim3(a.workers), dim3(kR32Threads), lds_bytes, stream,
+  hipLaunchKernelGGL((decode_rows32_kernel<kFp8, kSparse>), dim3(a.workers), dim3(kR32Threads), lds_bytes, stream,
                      reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const char*>(a.kv), a.kv_scales,
-                     a.block_table, a.plan, a.ws, a.out, a.lse, scalars_of(a));
+                     a.block_table, a.plan, a.ws, a.out, a.lse, srows, srow_stride, scalars_of(a));
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_rows32(const DecodeArgs& a, bool fp8, hipStream_t stream) {
-  return fp8 ? launch_rows32<true>(a, stream) : launch_rows32<false>(a, stream);
+  return fp8 ? launch_rows32<true, false>(a, nullptr, 0, stream) : launch_rows32<false, false>(a, nullptr, 0, stream);
+}
+
+hipError_t launch_decode_sparse_fp8(const DecodeArgs& a, const int32_t* rows, int row_stride, hipStream_t stream) {
+  return launch_rows32<true, true>(a, rows, row_stride, stream);
 }
 
 hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream) {

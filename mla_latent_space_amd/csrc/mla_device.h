@@ -72,6 +72,16 @@ __device__ __forceinline__ void lds_dma_x4(uint32_t lds_addr, uint32_t voff, i32
       : "m0");
 }
 
+// The same with 64 lanes x 4 B (LDS at m0 + 4 * lane).
+__device__ __forceinline__ void lds_dma_x1(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
+      : "m0");
+}
+
 // Work-group barrier for LDS traffic only. __syncthreads() also orders the LDS-DMA loads
 // still in flight (it waits vmcnt(0)), which would drain the prefetch ring at every
 // barrier; here each wave waits for exactly the DMA steps it needs (wait_vmcnt) and this

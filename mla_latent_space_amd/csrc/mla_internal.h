@@ -76,6 +76,15 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode_rows32(const DecodeArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_decode_sparse_fp8(const DecodeArgs& a, const int32_t* rows, int row_stride, hipStream_t stream);
+hipError_t launch_sparse_rows(const int32_t* indices, int topk, const int32_t* block_table, int max_pages,
+                              const int32_t* seqlens, int batch, int s_q, int64_t num_pages, int32_t* rows,
+                              int stride, int32_t* vis, hipStream_t stream);
+// token-sparse decode: row lists [batch * s_q, stride] (stride = topk rounded up to 32), then
+// the visible counts [batch * s_q]
+inline int sparse_stride(int topk) { return (topk + 31) / 32 * 32; }
+constexpr int kSparseHeads = 128;   // one 128-row tile per query token
+constexpr int kSparseMaxTopk = 1 << 20;
 hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream);
 struct HybridArgs {
   const void *q_nope, *q_rope, *k_new, *kr_new, *v_new;

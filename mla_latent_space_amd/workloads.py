@@ -202,3 +202,36 @@ def make_config(name: str, seed: Optional[int] = None) -> Workload:
     c.pop("seed", None)
     return make_workload(name, seed=s, **c)
 
+
+
+def make_sparse_indices(seqlens, s_q: int, topk: int, seed: int, fill: float = 1.0, pad_frac: float = 0.0,
+                        dup_frac: float = 0.0) -> np.ndarray:
+    """Seeded top-k token lists for a token-sparse decode: int32 [b, s_q, topk]. For query token
+    (i, j) the list holds round(fill * min(topk, t_i)) distinct positions of sequence i drawn
+    uniformly without replacement, in random order; a fraction ``dup_frac`` of them is then
+    overwritten with copies of other kept positions, and a fraction ``pad_frac`` of all entries
+    with padding (-1 or a position >= t_i); the rest of the list is -1. (A CPU
+    torch.Generator seeded with ``seed``; draws in (i, j) order.)"""
+    gen = torch.Generator().manual_seed(seed)
+    lens = np.asarray(seqlens, dtype=np.int64)
+    b = lens.shape[0]
+    out = np.full((b, s_q, topk), -1, dtype=np.int32)
+    for i in range(b):
+        t = int(lens[i])
+        for j in range(s_q):
+            k = int(round(fill * min(topk, t)))
+            if k > 0:
+                pos = torch.randperm(t, generator=gen)[:k].numpy().astype(np.int32)
+                nd = int(dup_frac * k)
+                if nd > 0 and k > 1:
+                    src = torch.randint(0, k, (nd,), generator=gen).numpy()
+                    dst = torch.randint(0, k, (nd,), generator=gen).numpy()
+                    pos[dst] = pos[src]
+                out[i, j, :k] = pos
+            npad = int(pad_frac * topk)
+            if npad > 0:
+                where = torch.randperm(topk, generator=gen)[:npad].numpy()
+                bad = np.where(torch.rand(npad, generator=gen).numpy() < 0.5, -1,
+                               t + torch.randint(0, 1000, (npad,), generator=gen).numpy()).astype(np.int32)
+                out[i, j, where] = bad
+    return out

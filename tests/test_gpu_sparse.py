@@ -1,0 +1,74 @@
+"""GPU parity of the token-level sparse decode over an fp8 cache (library card page "FlashMLA:
+Efficient Multi-head Latent Attention Kernels": sparse attention over selected tokens in
+decoding) against the fp64 oracle, through the C ABI: lists shorter and longer than a
+32-token step, random order, duplicates, padding entries, empty lists, query tokens of one
+sequence with different lists, several worker counts (split lists), a bitwise repeat, and
+sampled rows at the full V3.2-like size. Held to the fp8 bounds of the dense decode."""
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_space_amd as mla
+from mla_latent_space_amd import workloads as wl
+from oracle import mla as om
+from tests.gpu_common import FP8_TOL, Dev, compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run(w, idx, num_workers=None):
+    d = Dev(w)
+    ind = torch.from_numpy(idx).cuda()
+    plan = mla.get_sparse_plan(ind, d.bt, d.sl, int(w.kv.shape[0]), w.heads, num_workers)
+    out, lse = mla.sparse_decode_fwd(d.q, d.kv, d.scales, w.scale, plan)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("topk,s_q,fill,pad,dup,W", [
+    (1, 1, 1.0, 0.0, 0.0, 256),
+    (31, 2, 1.0, 0.0, 0.0, 7),
+    (33, 1, 0.7, 0.2, 0.0, 256),
+    (100, 4, 1.0, 0.1, 0.1, 1),
+    (300, 2, 0.5, 0.05, 0.05, 5),
+    (2048, 1, 1.0, 0.0, 0.0, 256),
+])
+def test_sparse_matches_oracle(topk, s_q, fill, pad, dup, W):
+    w = wl.make_workload("sparse", batch=4, s_q=s_q, heads=128, seqlens=[5, 64, 700, 2100], kv_dtype="fp8",
+                         seed=70 + topk + s_q)
+    idx = wl.make_sparse_indices(w.seqlens, s_q, topk, seed=80 + topk, fill=fill, pad_frac=pad, dup_frac=dup)
+    _say("sparse topk", topk, "s_q", s_q, "W", W)
+    out, lse = _run(w, idx, W)
+    ro, rl = om.decode_sparse(w.q, w.kv, w.kv_scales, "fp8", w.block_table, w.seqlens, idx, w.scale)
+    compare(out, lse, ro, rl, FP8_TOL, f"sparse topk={topk} s_q={s_q} W={W}")
+
+
+def test_sparse_empty_lists_and_bitwise_repeat():
+    w = wl.make_workload("sparse-empty", batch=3, s_q=2, heads=128, seqlens=[0, 10, 300], kv_dtype="fp8", seed=91)
+    idx = wl.make_sparse_indices(w.seqlens, 2, 64, seed=92)
+    idx[1, 0, :] = -1                       # an all-padding list
+    idx[2, 1, :] = 5000                     # positions past the sequence
+    _say("sparse empty + repeat")
+    o1, l1 = _run(w, idx, 13)
+    o2, l2 = _run(w, idx, 13)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    for (i, j) in ((0, 0), (0, 1), (1, 0), (2, 1)):
+        assert np.all(o1[i, j] == 0) and np.all(np.isneginf(l1[i, j]))
+    ro, rl = om.decode_sparse(w.q, w.kv, w.kv_scales, "fp8", w.block_table, w.seqlens, idx, w.scale)
+    compare(o1, l1, ro, rl, FP8_TOL, "sparse empty")
+
+
+def test_sparse_full_size_sampled():
+    """64 sequences of 32,768 fp8 tokens, 2,048 selected tokens per query token; every row of
+    three sequences against the oracle."""
+    w = wl.make_config("fp8")
+    idx = wl.make_sparse_indices(w.seqlens, w.s_q, 2048, seed=93)
+    _say("sparse full size")
+    out, lse = _run(w, idx)
+    seqs = [0, 31, 63]
+    ro, rl = om.decode_sparse(w.q, w.kv, w.kv_scales, "fp8", w.block_table, w.seqlens, idx, w.scale, seqs=seqs)
+    compare(out[seqs], lse[seqs], ro[seqs], rl[seqs], FP8_TOL, "sparse full size")
