@@ -219,6 +219,69 @@ def hybrid(steps: int, warmup: int, b: int = 32, s_q: int = 16, heads: int = 128
                                     "hybrid": round(bound(hyb_flops, hyb_bytes), 1)}}
 
 
+def sparse(steps: int, warmup: int, b: int = 64, t: int = 32768, topk: int = 2048, heads: int = 128):
+    """Token-level sparse decode over an fp8 cache at a DeepSeek-V3.2-like shape: b=64 sequences
+    of t=32,768 cached tokens (s=1, h=128), each query token attending to its own 2,048 selected
+    tokens (a seeded uniform choice without replacement, in random order). One step = the row
+    lists and split plan (mla_get_sparse_plan) and the decode (mla_sparse_decode_fwd). Seeded
+    random codes (NaN codes excluded), scales and rope values generated on the device."""
+    import numpy as np
+    import torch
+    import mla_latent_space_amd as mla
+    dev = "cuda"
+    gen = torch.Generator(device=dev).manual_seed(21)
+    per = t // 64
+    pages = b * per
+    codes = torch.randint(0, 256, (pages, 64, 512), generator=gen, device=dev, dtype=torch.int32)
+    codes = torch.where((codes & 0x7F) == 0x7F, torch.zeros_like(codes), codes).to(torch.uint8)
+    rope = torch.randn((pages, 64, 64), generator=gen, device=dev).to(torch.bfloat16).view(torch.uint8)
+    kv = torch.cat([codes, rope], dim=2).contiguous()
+    del codes, rope
+    scales = (torch.rand((pages, 64, 4), generator=gen, device=dev) * 0.01 + 1e-3).contiguous()
+    bt = torch.randperm(pages, generator=gen, device=dev).to(torch.int32).view(b, per).contiguous()
+    sl = torch.full((b,), t, dtype=torch.int32, device=dev)
+    idx = torch.stack([torch.randperm(t, generator=gen, device=dev)[:topk] for _ in range(b)]).to(torch.int32)
+    idx = idx.view(b, 1, topk).contiguous()
+    q = torch.randn((b, 1, heads, 576), generator=gen, device=dev).to(torch.bfloat16)
+    scale = (128 + 64) ** -0.5
+    W = mla.default_num_workers(0)
+    ws = torch.empty(max(mla.workspace_bytes(b, 1, heads, W), 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((b, 1, heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((b, 1, heads), dtype=torch.float32, device=dev)
+    plan = mla.get_sparse_plan(idx, bt, sl, pages, heads, W)
+
+    def step(i):
+        mla.get_sparse_plan(idx, bt, sl, pages, heads, W)
+        mla.sparse_decode_fwd(q, kv, scales, scale, plan, workspace=ws, out=out, lse=lse)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    step_us = (time.perf_counter() - t0) / steps * 1e6
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        mla.sparse_decode_fwd(q, kv, scales, scale, plan, workspace=ws, out=out, lse=lse)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec_us = float(np.mean([a.elapsed_time(c) * 1e3 for a, c in ev]))
+    rows = b * heads
+    byts = float(b * topk * (512 + 128 + 16) + b * topk * 4 + rows * 576 * 2 + rows * (512 + 1) * 4)
+    flops = 2.0 * rows * topk * (2 * K_LAT + P_ROPE)
+    tf = flops / (dec_us * 1e-6) / 1e12
+    bound_us = max(flops / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBPS * 1e9)) * 1e6
+    return {"workload": f"b={b} s=1 h={heads} t={t} fp8 cache, top-{topk} tokens per query token",
+            "step_us": round(step_us, 2), "decode_us": round(dec_us, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "bytes": byts, "flops": flops,
+                         "bound_us": round(bound_us, 2)}}
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle (as is) over the workload's sequences, one at a time, until ~budget_s of
     host time (whole passes over the batch are repeated if one pass is shorter), scaled to
@@ -261,6 +324,7 @@ def main():
                     help="skip timing the query-absorption and output-decompression kernels")
     ap.add_argument("--no-hybrid", action="store_true",
                     help="skip the split latent + decompressed variant's leg")
+    ap.add_argument("--no-sparse", action="store_true", help="skip the token-sparse fp8 decode's leg")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times (the reference "
                          "kernel for scaling HBM byte counters), print its size and exit")
@@ -386,6 +450,8 @@ def main():
         rec["projections"] = projections(w, args.steps, min(args.warmup, 50))
     if w.kv_dtype == "bf16" and not args.no_hybrid:
         rec["hybrid"] = hybrid(min(args.steps, 50), min(args.warmup, 20))
+    if w.kv_dtype == "bf16" and not args.no_sparse:
+        rec["sparse"] = sparse(min(args.steps, 100), min(args.warmup, 50))
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -23,7 +23,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"mla_get_split_plan", "mla_decode_fwd", "mla_plan_bytes", "mla_workspace_bytes", "mla_absorb_query",
-            "mla_decompress_output", "mla_hybrid_merge"} <= set(names)
+            "mla_decompress_output", "mla_hybrid_merge", "mla_get_sparse_plan", "mla_sparse_decode_fwd",
+            "mla_sparse_rows_bytes"} <= set(names)
     L = ctypes.CDLL(mla.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -137,3 +138,37 @@ def test_hybrid_merge_rejects_bad_arguments_before_launch():
     assert b"n_new >= s_q" in L.mla_last_error_message()
     assert call(out=f + 4) == 1
     assert b"16-byte aligned" in L.mla_last_error_message()
+
+
+def test_sparse_calls_reject_bad_arguments_before_launch():
+    """Status codes and sizes of the token-sparse calls, returned before anything is enqueued
+    (fake, never dereferenced device addresses; no GPU needed)."""
+    L = mla.lib()
+    f = 1 << 20
+    assert L.mla_sparse_rows_bytes(2, 3, 40) == ((2 * 3 * 64 + 2 * 3) * 4 + 15) // 16 * 16
+    assert L.mla_sparse_rows_bytes(0, 3, 40) == 0 and L.mla_sparse_rows_bytes(2, 3, 0) == 0
+
+    def plan(indices=f, topk=64, max_pages=8, batch=2, s_q=1, heads=128, pages=100, W=8, rows_bytes=1 << 20,
+             plan_bytes=1 << 20, rows=f):
+        return L.mla_get_sparse_plan(indices, topk, f, max_pages, f, batch, s_q, heads, pages, W, rows, rows_bytes, f,
+                                     plan_bytes, None)
+
+    assert plan(indices=None) == 1
+    assert plan(topk=0) == 1 and plan(batch=0) == 1 and plan(pages=0) == 1 and plan(max_pages=0) == 1
+    assert plan(heads=64) == 2                          # one 128-row tile per query token
+    assert plan(pages=60000) == 2                       # 31-bit row offsets
+    assert b"num_pages" in L.mla_last_error_message()
+    assert plan(rows_bytes=16) == 3 and plan(plan_bytes=16) == 3
+    assert plan(rows=f + 4) == 1
+
+    def dec(kv_dtype=1, q=f, scales=f, heads=128, scale=0.1, ws_bytes=1 << 30, out=f):
+        return L.mla_sparse_decode_fwd(q, f, scales, kv_dtype, 100, 2, 1, heads, 64, scale, f, f, 8, f, ws_bytes, out,
+                                       f, None)
+
+    assert dec(kv_dtype=0) == 2                         # bf16 cache: not on this path
+    assert dec(kv_dtype=7) == 1
+    assert dec(q=None) == 1 and dec(scales=None) == 1
+    assert dec(heads=16) == 2
+    assert dec(scale=-1.0) == 1
+    assert dec(ws_bytes=16) == 3
+    assert dec(out=f + 8) == 1
