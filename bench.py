@@ -322,9 +322,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-projections", action="store_true",
                     help="skip timing the query-absorption and output-decompression kernels")
-    ap.add_argument("--no-hybrid", action="store_true",
-                    help="skip the split latent + decompressed variant's leg")
-    ap.add_argument("--no-sparse", action="store_true", help="skip the token-sparse fp8 decode's leg")
+    ap.add_argument("--hybrid", action="store_true",
+                    help="also time the split latent + decompressed variant (its latent part runs the same decode "
+                         "kernel, so it stays out of the default run's kernel trace)")
+    ap.add_argument("--sparse", action="store_true", help="also time the token-sparse fp8 decode")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times (the reference "
                          "kernel for scaling HBM byte counters), print its size and exit")
@@ -448,9 +449,9 @@ def main():
     }
     if w.kv_dtype == "bf16" and not args.no_projections:
         rec["projections"] = projections(w, args.steps, min(args.warmup, 50))
-    if w.kv_dtype == "bf16" and not args.no_hybrid:
+    if args.hybrid:
         rec["hybrid"] = hybrid(min(args.steps, 50), min(args.warmup, 20))
-    if w.kv_dtype == "bf16" and not args.no_sparse:
+    if args.sparse:
         rec["sparse"] = sparse(min(args.steps, 100), min(args.warmup, 50))
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
