@@ -9,40 +9,71 @@
 // count becomes that query token's visible length for the split plan, which then treats each
 // query token as a sequence of one query row per head.
 //
-// One wave per query token; 64 entries per pass, packed with a ballot and a lane prefix count.
+// One 256-thread work-group per query token. The list is taken in blocks of 2,048 entries, 8
+// consecutive ones per thread, so that a block's index loads and then its block-table loads
+// are all in flight at once; a work-group prefix sum over the per-thread key counts (a shuffle
+// scan within each wave, then the four wave totals through LDS) places every thread's keys,
+// which keeps list order.
 #include "mla_device.h"
 
 namespace mla {
 namespace {
 
-__global__ __launch_bounds__(64) void sparse_rows_kernel(const int32_t* __restrict__ indices, int topk,
-                                                         const int32_t* __restrict__ block_table, int max_pages,
-                                                         const int32_t* __restrict__ seqlens, int s_q,
-                                                         int64_t num_pages, int32_t* __restrict__ rows, int stride,
-                                                         int32_t* __restrict__ vis) {
-  const int v = blockIdx.x, i = v / s_q, lane = threadIdx.x;
+constexpr int kSrThreads = 256;
+constexpr int kSrPer = 8;   // consecutive entries per thread and block
+
+__global__ __launch_bounds__(kSrThreads) void sparse_rows_kernel(const int32_t* __restrict__ indices, int topk,
+                                                                 const int32_t* __restrict__ block_table,
+                                                                 int max_pages, const int32_t* __restrict__ seqlens,
+                                                                 int s_q, int64_t num_pages, int32_t* __restrict__ rows,
+                                                                 int stride, int32_t* __restrict__ vis) {
+  __shared__ int wave_tot[4];
+  const int v = blockIdx.x, i = v / s_q, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int t = seqlens[i];
   const int cap = max_pages * kPage;
   t = t < cap ? t : cap;
   const int32_t* src = indices + (int64_t)v * topk;
   int32_t* dst = rows + (int64_t)v * stride;
-  int kept = 0;
-  for (int e0 = 0; e0 < topk; e0 += 64) {
-    const int e = e0 + lane;
-    const int u = e < topk ? src[e] : -1;
-    const bool key = u >= 0 && u < t;
-    int32_t stored = 0;
-    if (key) {
-      const int pid = block_table[(int64_t)i * max_pages + (u >> 6)];
-      if (pid >= 0 && (int64_t)pid < num_pages) stored = pid * kPage + (u & (kPage - 1)) + 1;
+  int kept = 0;   // keys placed by the earlier blocks (the same in every thread)
+  for (int e0 = 0; e0 < topk; e0 += kSrThreads * kSrPer) {
+    int u[kSrPer], stored[kSrPer];
+#pragma unroll
+    for (int r = 0; r < kSrPer; ++r) {
+      const int e = e0 + kSrPer * tid + r;
+      u[r] = e < topk ? src[e] : -1;
     }
-    const uint64_t mask = __ballot(key);
-    const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-    if (key) dst[kept + before] = stored;
-    kept += __popcll(mask);
+    int mine = 0;
+#pragma unroll
+    for (int r = 0; r < kSrPer; ++r) {
+      const bool key = u[r] >= 0 && u[r] < t;
+      stored[r] = -1;   // (not a key)
+      if (key) {
+        const int pid = block_table[(int64_t)i * max_pages + (u[r] >> 6)];
+        stored[r] = (pid >= 0 && (int64_t)pid < num_pages) ? pid * kPage + (u[r] & (kPage - 1)) + 1 : 0;
+        ++mine;
+      }
+    }
+    // exclusive prefix of `mine` over the work-group
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int before = incl - mine;
+    for (int w = 0; w < wave; ++w) before += wave_tot[w];
+    const int block_tot = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+    __syncthreads();   // (wave_tot is rewritten by the next block)
+    int pos = kept + before;
+#pragma unroll
+    for (int r = 0; r < kSrPer; ++r)
+      if (stored[r] >= 0) dst[pos++] = stored[r];
+    kept += block_tot;
   }
-  for (int e = kept + lane; e < stride; e += 64) dst[e] = 0;
-  if (lane == 0) vis[v] = kept;
+  for (int e = kept + tid; e < stride; e += kSrThreads) dst[e] = 0;
+  if (tid == 0) vis[v] = kept;
 }
 
 }  // namespace
@@ -50,7 +81,7 @@ __global__ __launch_bounds__(64) void sparse_rows_kernel(const int32_t* __restri
 hipError_t launch_sparse_rows(const int32_t* indices, int topk, const int32_t* block_table, int max_pages,
                               const int32_t* seqlens, int batch, int s_q, int64_t num_pages, int32_t* rows,
                               int stride, int32_t* vis, hipStream_t stream) {
-  hipLaunchKernelGGL(sparse_rows_kernel, dim3(batch * s_q), dim3(64), 0, stream, indices, topk, block_table,
+  hipLaunchKernelGGL(sparse_rows_kernel, dim3(batch * s_q), dim3(kSrThreads), 0, stream, indices, topk, block_table,
                      max_pages, seqlens, s_q, num_pages, rows, stride, vis);
   return hipGetLastError();
 }
