@@ -67,3 +67,24 @@ def compare(out, lse, ref_out, ref_lse, tol, what=""):
             f.write(msg + "\n")
     assert rel <= tol["rel_l2"] and mabs <= tol["max_abs"] and dl <= tol["lse"], msg
     return rel, mabs, dl
+
+
+def fp8_rope_ramp(w, heads_aligned=16, q_val=64.0):
+    """Scores that grow along the sequence by hundreds of log2 units, on an fp8 cache through
+    its bf16 rope channels (bytes 512..639 of a row): heads 0..15 put q_val on the 64 rope
+    channels of the query, and every cached rope channel rises by j / (t - 1) at token j."""
+    def to_f32(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).float().numpy()
+
+    def to_bits(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(
+            torch.int16).numpy().view(np.uint16)
+
+    q = to_f32(w.q)
+    q[:, :, :heads_aligned, 512:] = q_val
+    w.q = to_bits(q)
+    rope = to_f32(np.ascontiguousarray(w.kv[..., 512:]).view(np.uint16))
+    for b, t in enumerate(w.seqlens):
+        for j in range(int(t)):
+            rope[w.block_table[b, j // 64], j % 64, :] += 1.0 * j / max(1, int(t) - 1)
+    w.kv[..., 512:] = to_bits(rope).view(np.uint8).reshape(w.kv[..., 512:].shape)

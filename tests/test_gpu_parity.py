@@ -10,7 +10,7 @@ from mla_latent_space_amd import workloads as wl
 from oracle import mla as om
 from oracle import plan as op
 
-from gpu_common import BF16_TOL, FP8_TOL, Dev, compare
+from gpu_common import BF16_TOL, FP8_TOL, Dev, compare, fp8_rope_ramp
 
 pytestmark = pytest.mark.gpu
 
@@ -168,6 +168,20 @@ def test_scores_growing_past_the_reference_window(W):
     out, lse = d.run(W)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, BF16_TOL, f"ramp W={W}")
+
+
+@pytest.mark.parametrize("W", [1, 256])
+def test_fp8_scores_growing_past_the_reference_window(W):
+    """The redo passes on the fp8 kernel, whose pipeline fill (staging, dequantisation) is its
+    own: the same growing scores through the cache's bf16 rope channels."""
+    w = wl.make_workload("ramp-fp8", batch=2, s_q=1, heads=32, seqlens=[600, 3000], kv_dtype="fp8", seed=33,
+                         poison=False)
+    fp8_rope_ramp(w)
+    _say("fp8 ramp W", W)
+    ro, rl = _oracle_all(w)
+    out, lse = Dev(w).run(W)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, FP8_TOL, f"fp8 ramp W={W}")
 
 
 def test_scores_growing_moderately_past_the_reference_window():

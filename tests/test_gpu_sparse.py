@@ -11,7 +11,7 @@ import torch
 import mla_latent_space_amd as mla
 from mla_latent_space_amd import workloads as wl
 from oracle import mla as om
-from tests.gpu_common import FP8_TOL, Dev, compare
+from tests.gpu_common import FP8_TOL, Dev, compare, fp8_rope_ramp
 
 pytestmark = pytest.mark.gpu
 
@@ -72,3 +72,19 @@ def test_sparse_full_size_sampled():
     seqs = [0, 31, 63]
     ro, rl = om.decode_sparse(w.q, w.kv, w.kv_scales, "fp8", w.block_table, w.seqlens, idx, w.scale, seqs=seqs)
     compare(out[seqs], lse[seqs], ro[seqs], rl[seqs], FP8_TOL, "sparse full size")
+
+
+@pytest.mark.parametrize("W", [1, 256])
+def test_sparse_scores_growing_past_the_reference_window(W):
+    """The redo passes on the token-sparse kernel (its own pipeline fill with the row ring):
+    scores that grow along the selected tokens by hundreds of log2 units, through the cache's
+    bf16 rope channels; full lists in random order."""
+    w = wl.make_workload("ramp-sparse", batch=2, s_q=1, heads=128, seqlens=[600, 3000], kv_dtype="fp8", seed=34,
+                         poison=False)
+    fp8_rope_ramp(w)
+    idx = wl.make_sparse_indices(w.seqlens, 1, 3000, seed=95)
+    _say("sparse ramp W", W)
+    out, lse = _run(w, idx, W)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ro, rl = om.decode_sparse(w.q, w.kv, w.kv_scales, "fp8", w.block_table, w.seqlens, idx, w.scale)
+    compare(out, lse, ro, rl, FP8_TOL, f"sparse ramp W={W}")
