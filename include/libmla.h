@@ -250,7 +250,8 @@ int32_t mla_sparse_decode_fwd(const void* q, const void* kv_cache, const float* 
  * out_old  device float32 [batch, s_q, heads, 128]: the old part's normalised output (the
  *          decompressed out of mla_decode_fwd); lse_old device float32 [batch, s_q, heads].
  * out      device float32 [batch, s_q, heads, 128]; lse device float32 [batch, s_q, heads].
- * batch, heads 1 .. 65535; s_q 1 .. 32; n_new 0 .. 2^24; with causal, n_new >= s_q.
+ * batch, heads 1 .. 65535; s_q 1 .. 32; n_new 0 .. 2^24 with (n_new + 32) * heads * 256 < 2^31;
+ * with causal, n_new >= s_q.
  * softmax_scale finite and > 0. All arrays but the lse ones 16-byte aligned and contiguous.
  * Stream-ordered; allocates nothing. Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
  * MLA_ERR_HIP. */

@@ -328,6 +328,8 @@ int32_t mla_hybrid_merge(const void* q_nope, const void* q_rope, const void* k_n
   if (s_q > 32) return fail(MLA_ERR_UNSUPPORTED, "s_q must be <= 32 (got %d)", s_q);
   if (batch > 65535 || heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch and heads must be <= 65535");
   if (n_new > (1 << 24)) return fail(MLA_ERR_UNSUPPORTED, "n_new must be <= 2^24 (got %d)", n_new);
+  if ((int64_t)(n_new + 32) * heads * 256 >= (1LL << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "(n_new + 32) * heads * 256 must be below 2^31 (31-bit offsets into k_new, v_new)");
   if (causal && n_new < s_q)
     return fail(MLA_ERR_UNSUPPORTED, "causal needs n_new >= s_q (got n_new %d, s_q %d): the old tokens must all "
                 "be visible", n_new, s_q);

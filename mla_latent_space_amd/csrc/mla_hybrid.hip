@@ -7,10 +7,11 @@
 //
 // One work-group of four waves per (sequence, head); all s_q <= 32 query rows of the head form
 // one 32-row MFMA tile (rows past s_q repeat row 0 and are not written). Wave w takes the new
-// tokens' 32-token chunks w, w+4, ...: the chunk's K rows (128 + 64 channels, 384 B) and V rows
-// are loaded into registers while the previous chunk is computed, then stored in the wave's
-// LDS area as 384-B rows with 16-B chunks XOR-swizzled by token, the layout whose operand reads
-// are free of bank conflicts. Per chunk: S^T[32 tokens x 32 rows] = K Q^T (12
+// tokens' 32-token chunks w, w+4, ...: each chunk is loaded straight into one of the wave's two
+// LDS buffers by LDS-DMA (two chunks in flight per wave), as three regions whose 16-B chunks are
+// XOR-swizzled by token so that the operand reads are free of bank conflicts: K (128 channels,
+// 256-B rows, chunk ^ u%16), the rope keys (128-B rows, chunk ^ (u/2)%8) and V (256-B rows,
+// chunk ^ 4(u%4)). Per chunk: S^T[32 tokens x 32 rows] = K Q^T (12
 // v_mfma_f32_32x32x16_bf16, Q^T in registers), mask, online softmax in the log2 domain with a
 // reference that moves only when a row's maximum passes it by more than 2^8, then
 // O[32 rows x 128] += P V (8 MFMAs; P is the score accumulator rounded to bf16, read as the A
@@ -23,21 +24,21 @@ namespace mla {
 namespace {
 
 constexpr int kHyThreads = 256;
-constexpr int kHyChunk = 32;                     // new tokens per chunk
-constexpr int kHyRow = 384;                      // LDS row: 128 + 64 channels of K (or 128 of V + pad)
-constexpr int kHyArea = 2 * kHyChunk * kHyRow;   // per wave: K rows, then V rows (24 KiB)
-constexpr int kHyAlpha = 4 * kHyArea;            // per wave: 32 rescale factors
-constexpr int kHyLds = kHyAlpha + 4 * 32 * 4;
-constexpr int kHyLoads = 20;                     // 16-B loads per lane and chunk: 12 of K, 8 of V
-static_assert(kHyRow % 256 == 128, "consecutive tokens alternate 128-B bank halves");
-constexpr int kHyObufRow = 160;                  // floats per partial O row in the merge (640 B)
-static_assert(4 * 32 * kHyObufRow * 4 + 4 * 32 * 8 <= kHyAlpha, "the merge area fits in the staging areas");
+constexpr int kHyChunk = 32;                      // new tokens per chunk
+constexpr int kHyR = kHyChunk * 256;              // buffer regions: K rows (256 B) at 0, rope rows (128 B),
+constexpr int kHyV = kHyR + kHyChunk * 128;       // V rows (256 B)
+constexpr int kHyBuf = kHyV + kHyChunk * 256;     // 20 KiB per chunk buffer
+constexpr int kHyArea = 2 * kHyBuf;               // per wave: two buffers
+constexpr int kHyLds = 4 * kHyArea;               // 160 KiB
+constexpr int kHyDma = 20;                        // LDS-DMA instructions per chunk and wave
+constexpr int kHyObufRow = 160;                   // floats per partial O row in the merge (640 B)
+static_assert(kHyLds <= 160 * 1024, "LDS budget");
+static_assert(4 * 32 * kHyObufRow * 4 + 4 * 32 * 8 <= kHyLds, "the merge area fits in the staging areas");
 
-__device__ __forceinline__ uint32_t hy_sw(uint32_t u) { return (((u >> 1) & 1u) << 2) | ((u >> 2) & 3u); }
-// LDS byte offset of logical 16-B chunk ch of token row u
-__device__ __forceinline__ uint32_t hy_pos(uint32_t u, uint32_t ch) {
-  return u * kHyRow + 16u * ((ch & ~7u) | ((ch & 7u) ^ hy_sw(u)));
-}
+// physical byte offset of logical 16-B chunk ch of token row u in each region
+__device__ __forceinline__ uint32_t hy_k(uint32_t u, uint32_t ch) { return u * 256u + 16u * (ch ^ (u & 15u)); }
+__device__ __forceinline__ uint32_t hy_r(uint32_t u, uint32_t ch) { return u * 128u + 16u * (ch ^ ((u >> 1) & 7u)); }
+__device__ __forceinline__ uint32_t hy_v(uint32_t u, uint32_t ch) { return u * 256u + 16u * (ch ^ (4u * (u & 3u))); }
 
 __global__ __launch_bounds__(kHyThreads, 1) void hybrid_new_kernel(
     const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_rope, const __bf16* __restrict__ k_new,
@@ -46,10 +47,11 @@ __global__ __launch_bounds__(kHyThreads, 1) void hybrid_new_kernel(
     float scale_log2, int causal) {
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   char __attribute__((address_space(3)))* lds = (char __attribute__((address_space(3)))*)smem_raw;
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t kbase = (uint32_t)wave * kHyArea, vbase = kbase + kHyChunk * kHyRow;
+  const uint32_t area = (uint32_t)wave * kHyArea;
   const int row = lane & 31, hl = lane >> 5;
 
   // Q^T B operand: lane holds query row l%32, channels 16ks + 8(l/32) .. +7 (ks 0..7 nope, 8..11 rope)
@@ -66,55 +68,44 @@ __global__ __launch_bounds__(kHyThreads, 1) void hybrid_new_kernel(
   // new tokens visible to this lane's row (0 for padding rows)
   const int lim = row < S ? (causal ? N - S + 1 + row : N) : 0;
 
-  // chunk loads: piece p = 64m + lane; K: token p / 24, chunk p % 24 (0..15 nope, 16..23 rope);
-  // V: token p / 16, chunk p % 16. Tokens past N read as zeros.
-  u32x4 st[kHyLoads];
-  auto load_chunk = [&](int c) {
-    const int tok0 = kHyChunk * c;
-#pragma unroll
-    for (int m = 0; m < 12; ++m) {
-      const int p = 64 * m + lane, tk = p / 24, ch = p % 24, u = tok0 + tk;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (u < N) {
-        const __bf16* src = ch < 16 ? k_new + (((int64_t)b * N + u) * H + h) * 128 + 8 * ch
-                                    : kr_new + ((int64_t)b * N + u) * 64 + 8 * (ch - 16);
-        v = *reinterpret_cast<const u32x4*>(src);
-      }
-      st[m] = v;
-    }
+  // buffer descriptors over sequence b's new tokens: K and V rows of head h at (u H + h) 256 B,
+  // rope rows at 128u B; tokens past N read as zeros (the host keeps N H 256 below 2^31)
+  const i32x4 rk = make_rsrc(reinterpret_cast<uint64_t>(k_new) + (uint64_t)b * N * H * 256, N * H * 256);
+  const i32x4 rv = make_rsrc(reinterpret_cast<uint64_t>(v_new) + (uint64_t)b * N * H * 256, N * H * 256);
+  const i32x4 rr = make_rsrc(reinterpret_cast<uint64_t>(kr_new) + (uint64_t)b * N * 128, N * 128);
+  // chunk c into buffer bf: instruction m of each region fills 1 KiB (K, V: 4 rows; rope: 8 rows);
+  // lane l lands at 16 l, which holds the logical chunk the region's swizzle puts there
+  auto dma_chunk = [&](int c, int bf) {
+    const uint32_t dst = lds_u32 + area + (uint32_t)bf * kHyBuf;
+    const uint32_t l = (uint32_t)lane;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const int p = 64 * m + lane, tk = p / 16, ch = p % 16, u = tok0 + tk;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (u < N) v = *reinterpret_cast<const u32x4*>(v_new + (((int64_t)b * N + u) * H + h) * 128 + 8 * ch);
-      st[12 + m] = v;
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int m = 0; m < 12; ++m) {
-      const int p = 64 * m + lane;
-      *(u32x4 __attribute__((address_space(3)))*)(lds + (kbase + hy_pos(p / 24, p % 24))) = st[m];
+      const uint32_t u = 4u * m + (l >> 4), un = (uint32_t)kHyChunk * c + u;
+      const uint32_t rowoff = (un * (uint32_t)H + (uint32_t)h) * 256u;
+      lds_dma_x4(dst + 1024u * m, rowoff + 16u * ((l & 15u) ^ (u & 15u)), rk);
+      lds_dma_x4(dst + kHyV + 1024u * m, rowoff + 16u * ((l & 15u) ^ (4u * (u & 3u))), rv);
     }
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int p = 64 * m + lane;
-      *(u32x4 __attribute__((address_space(3)))*)(lds + (vbase + hy_pos(p / 16, p % 16))) = st[12 + m];
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t u = 8u * m + (l >> 3), un = (uint32_t)kHyChunk * c + u;
+      lds_dma_x4(dst + kHyR + 1024u * m, un * 128u + 16u * ((l & 7u) ^ ((u >> 1) & 7u)), rr);
     }
   };
-  // operand reads: K rows (lane: token l%32, logical chunk 2ks + l/32); V^T tile (q, c): tokens
-  // 16q + 8e + 4(G/2) + j/4 and channels 32c + 16(G%2) + 4(j%4) .. +3 for lane (G, j) = (l/16, l%16)
-  auto k_read = [&](int ks) -> bf16x8 {
-    return lds_b128(lds + (kbase + hy_pos((uint32_t)row, (uint32_t)(2 * ks + hl))));
+  // operand reads: K rows (lane: token l%32, logical chunk 2ks + l/32 of the 192 channels); V^T
+  // tile (q, c): tokens 16q + 8e + 4(G/2) + j/4 and channels 32c + 16(G%2) + 4(j%4) .. +3 for
+  // lane (G, j) = (l/16, l%16)
+  auto k_read = [&](uint32_t base, int ks) -> bf16x8 {
+    const uint32_t ch = (uint32_t)(2 * ks + hl);
+    return lds_b128(lds + (ks < 8 ? base + hy_k((uint32_t)row, ch) : base + kHyR + hy_r((uint32_t)row, ch - 16u)));
   };
-  auto v_read = [&](int q, int c) -> bf16x8 {
+  auto v_read = [&](uint32_t base, int q, int c) -> bf16x8 {
     const uint32_t G = (uint32_t)lane >> 4, j = (uint32_t)lane & 15u;
     bf16x4 part[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const uint32_t u = 16u * q + 8u * e + 4u * (G >> 1) + (j >> 2);
       const uint32_t ch = 4u * c + 2u * (G & 1u) + ((j >> 1) & 1u);
-      part[e] = lds_tr16(lds + (vbase + hy_pos(u, ch) + 8u * (j & 1u)));
+      part[e] = lds_tr16(lds + (base + kHyV + hy_v(u, ch) + 8u * (j & 1u)));
     }
     return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
   };
@@ -126,16 +117,17 @@ __global__ __launch_bounds__(kHyThreads, 1) void hybrid_new_kernel(
   float l_run = 0.f;
   const int nchunks = (N + kHyChunk - 1) / kHyChunk;
   bool first = true;
-  float __attribute__((address_space(3)))* alpha_s =
-      (float __attribute__((address_space(3)))*)(lds + kHyAlpha + 128 * wave);
-  if (wave < nchunks) load_chunk(wave);
+  // this wave's chunks c = wave + 4k go to buffer k % 2, two in flight
+  if (wave < nchunks) dma_chunk(wave, 0);
+  if (wave + 4 < nchunks) dma_chunk(wave + 4, 1);
 #pragma unroll 1
-  for (int c = wave; c < nchunks; c += 4) {
-    store_chunk();   // (after this wave's reads of the previous chunk: LDS keeps a wave's order)
-    if (c + 4 < nchunks) load_chunk(c + 4);
+  for (int c = wave, k = 0; c < nchunks; c += 4, ++k) {
+    if (c + 4 < nchunks) wait_vmcnt<kHyDma>();   // chunk c landed (c + 4 may stay in flight)
+    else wait_vmcnt<0>();
+    const uint32_t base = area + (uint32_t)(k & 1) * kHyBuf;
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 12; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_read(ks), qb[ks], s, 0, 0, 0);
+    for (int ks = 0; ks < 12; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_read(base, ks), qb[ks], s, 0, 0, 0);
     // mask (register r: token 32c + 8(r/4) + 4(l/32) + r%4) and the row maximum
     const int key0 = kHyChunk * c + 4 * hl;
     float mx = -INFINITY;
@@ -155,7 +147,9 @@ __global__ __launch_bounds__(kHyThreads, 1) void hybrid_new_kernel(
     const float alpha = move ? (m_ref == -INFINITY ? 0.f : exp2f(m_ref - new_ref)) : 1.f;
     if (__ballot(move) != 0) {   // (wave-uniform)
       l_run *= alpha;
-      if (!first) {   // O rows live in other lanes: their factors go through LDS
+      if (!first) {   // O rows live in other lanes: their factors go through LDS (the K rows, read by now)
+        float __attribute__((address_space(3)))* alpha_s = (float __attribute__((address_space(3)))*)(lds + base);
+        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // (the K reads first)
         if (lane < 32) alpha_s[lane] = alpha;
         f32x4 a4[4];
 #pragma unroll
@@ -186,8 +180,15 @@ __global__ __launch_bounds__(kHyThreads, 1) void hybrid_new_kernel(
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pk[q], v_read(q, t), o[t], 0, 0, 0);
+      for (int t = 0; t < 4; ++t)
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pk[q], v_read(base, q, t), o[t], 0, 0, 0);
+    // the buffer's next chunk, once this chunk's LDS reads are done
+    if (c + 8 < nchunks) {
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+      dma_chunk(c + 8, k & 1);
+    }
   }
+  wait_vmcnt<0>();
 
   // ---- merge: the four waves' partials (relative to their references) and the old part
   __syncthreads();   // every wave is done with its staging area

@@ -136,6 +136,8 @@ def test_hybrid_merge_rejects_bad_arguments_before_launch():
     assert call(batch=65536) == 2
     assert call(n=3, s_q=4, causal=1) == 2              # causal needs n >= s_q
     assert b"n_new >= s_q" in L.mla_last_error_message()
+    assert call(n=70000, heads=128) == 2                # 31-bit offsets into the new tokens
+    assert b"2^31" in L.mla_last_error_message()
     assert call(out=f + 4) == 1
     assert b"16-byte aligned" in L.mla_last_error_message()
 
