@@ -7,8 +7,9 @@
 //
 // One work-group of four waves per (sequence, head); all s_q <= 32 query rows of the head form
 // one 32-row MFMA tile (rows past s_q repeat row 0 and are not written). Wave w takes the new
-// tokens' 32-token chunks w, w+4, ...: each chunk is loaded straight into one of the wave's two
-// LDS buffers by LDS-DMA (two chunks in flight per wave), as three regions whose 16-B chunks are
+// tokens' 32-token chunks w, w+4, ...: each chunk is loaded straight into the wave's LDS buffer
+// by LDS-DMA (80 KiB per work-group, so that a second work-group on the CU streams while this
+// one waits, starts or merges), as three regions whose 16-B chunks are
 // XOR-swizzled by token so that the operand reads are free of bank conflicts: K (128 channels,
 // 256-B rows, chunk ^ u%16), the rope keys (128-B rows, chunk ^ (u/2)%8) and V (256-B rows,
 // chunk ^ 4(u%4)). Per chunk: S^T[32 tokens x 32 rows] = K Q^T (12
@@ -28,10 +29,10 @@ constexpr int kHyChunk = 32;                      // new tokens per chunk
 constexpr int kHyR = kHyChunk * 256;              // buffer regions: K rows (256 B) at 0, rope rows (128 B),
 constexpr int kHyV = kHyR + kHyChunk * 128;       // V rows (256 B)
 constexpr int kHyBuf = kHyV + kHyChunk * 256;     // 20 KiB per chunk buffer
-constexpr int kHyArea = 2 * kHyBuf;               // per wave: two buffers
-constexpr int kHyLds = 4 * kHyArea;               // 160 KiB
+constexpr int kHyArea = kHyBuf;                   // per wave: one buffer
+constexpr int kHyLds = 4 * kHyArea;               // 80 KiB: two work-groups per CU
 constexpr int kHyDma = 20;                        // LDS-DMA instructions per chunk and wave
-constexpr int kHyObufRow = 160;                   // floats per partial O row in the merge (640 B)
+constexpr int kHyObufRow = 132;                   // floats per partial O row in the merge (528 B)
 static_assert(kHyLds <= 160 * 1024, "LDS budget");
 static_assert(4 * 32 * kHyObufRow * 4 + 4 * 32 * 8 <= kHyLds, "the merge area fits in the staging areas");
 
@@ -40,7 +41,7 @@ __device__ __forceinline__ uint32_t hy_k(uint32_t u, uint32_t ch) { return u * 2
 __device__ __forceinline__ uint32_t hy_r(uint32_t u, uint32_t ch) { return u * 128u + 16u * (ch ^ ((u >> 1) & 7u)); }
 __device__ __forceinline__ uint32_t hy_v(uint32_t u, uint32_t ch) { return u * 256u + 16u * (ch ^ (4u * (u & 3u))); }
 
-__global__ __launch_bounds__(kHyThreads, 1) void hybrid_new_kernel(
+__global__ __launch_bounds__(kHyThreads, 2) void hybrid_new_kernel(
     const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_rope, const __bf16* __restrict__ k_new,
     const __bf16* __restrict__ kr_new, const __bf16* __restrict__ v_new, const float* __restrict__ out_old,
     const float* __restrict__ lse_old, float* __restrict__ out, float* __restrict__ lse, int S, int N, int H,
@@ -117,14 +118,13 @@ __global__ __launch_bounds__(kHyThreads, 1) void hybrid_new_kernel(
   float l_run = 0.f;
   const int nchunks = (N + kHyChunk - 1) / kHyChunk;
   bool first = true;
-  // this wave's chunks c = wave + 4k go to buffer k % 2, two in flight
+  // this wave's chunks c = wave + 4k, one in flight (the other work-group on the CU covers the
+  // wait)
   if (wave < nchunks) dma_chunk(wave, 0);
-  if (wave + 4 < nchunks) dma_chunk(wave + 4, 1);
 #pragma unroll 1
   for (int c = wave, k = 0; c < nchunks; c += 4, ++k) {
-    if (c + 4 < nchunks) wait_vmcnt<kHyDma>();   // chunk c landed (c + 4 may stay in flight)
-    else wait_vmcnt<0>();
-    const uint32_t base = area + (uint32_t)(k & 1) * kHyBuf;
+    wait_vmcnt<0>();
+    const uint32_t base = area;
     f32x16 s = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_read(base, ks), qb[ks], s, 0, 0, 0);
@@ -183,9 +183,9 @@ __global__ __launch_bounds__(kHyThreads, 1) void hybrid_new_kernel(
       for (int t = 0; t < 4; ++t)
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pk[q], v_read(base, q, t), o[t], 0, 0, 0);
     // the buffer's next chunk, once this chunk's LDS reads are done
-    if (c + 8 < nchunks) {
+    if (c + 4 < nchunks) {
       __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-      dma_chunk(c + 8, k & 1);
+      dma_chunk(c + 4, 0);
     }
   }
   wait_vmcnt<0>();
