@@ -779,8 +779,13 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
               if (t >= 18 && t < 26 && !(t & 1)) bz0[(t - 18) >> 1] = pv_read(pa, (t - 18) >> 1);
               if (t == 0) mfma_v0(s, cur, qreg[0]);
               else mfma_v(s, cur, t >= 34 ? qx[t - 34] : qreg[t]);
-              if (kSparse && (t & 3) == 1 && t < 24) f8_sv = f8_row(t >> 2);   // (two MFMAs ahead)
-              if ((t & 3) == 3 && t < 24) dma_f8(rs, lslot, t >> 2, f8_sv);
+              // DMA instruction j at t = 2j + 1 (token-sparse: the row of the next one read right
+              // after, two MFMAs ahead of its use)
+              if (kSparse && t == 0) f8_sv = f8_row(0);
+              if ((t & 1) == 1 && t < 12) {
+                dma_f8(rs, lslot, t >> 1, f8_sv);
+                if (kSparse && t < 11) f8_sv = f8_row((t >> 1) + 1);
+              }
               if (t == 27) dma_rows((row_slot + 2) & 3);   // token-sparse: rows of step i+6
               if (t == 14) f8_piece(0, 0);
               if (t == 15) f8_piece(0, 1);
