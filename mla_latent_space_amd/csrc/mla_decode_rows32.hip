@@ -463,10 +463,12 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   // Token-sparse: first the row numbers of steps g0 .. g0+3 (row ring slots 0..3), and of
   // g0+4, g0+5 into slots 0, 1 once the loads of g0, g0+1 have read them; afterwards row_slot
   // is 0 (step g0+4) and region i loads the rows of step i+6 into the slot two ahead.
-  auto f8_fill = [&]() {
+  auto f8_fill = [&](bool rows_loaded) {
     if constexpr (kSparse) {
+      if (!rows_loaded) {
 #pragma unroll 1
-      for (int r = 0; r < 4; ++r) dma_rows(r);
+        for (int r = 0; r < 4; ++r) dma_rows(r);
+      }
       wait_vmcnt<0>();
       barrier_lds();
       issue_step();
@@ -498,6 +500,12 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       barrier_lds();
     }
   };
+  // token-sparse: the row numbers of the first four steps go first (the row ring lies outside
+  // the area the queries are staged through), so that their latency hides under the staging
+  if constexpr (kSparse) {
+#pragma unroll 1
+    for (int r = 0; r < 4; ++r) dma_rows(r);
+  }
   // Start-up: the first item's 128 query rows (147 KB, contiguous in q) are staged through
   // the four ring slots by LDS-DMA, 32 rows per slot in the cache-step layout, and each wave
   // reads its 32 rows back with the score-operand read pattern. (Loaded straight into
@@ -527,7 +535,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     barrier_lds();   // every wave holds its rows before the ring is refilled
   }
   if constexpr (kFp8) {
-    f8_fill();
+    f8_fill(true);
   } else {
 #pragma unroll 1
     for (int i = 0; i < kR32Slots - 1; ++i) issue_step();
@@ -950,7 +958,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       load_slot = 0;
       comp_slot = 0;
       if constexpr (kFp8) {
-        f8_fill();
+        f8_fill(false);
       } else {
 #pragma unroll 1
         for (int j = 0; j < kR32Slots - 1; ++j) issue_step();
