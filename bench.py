@@ -331,8 +331,8 @@ def main():
                          "kernel for scaling HBM byte counters), print its size and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build measures the single-GPU decode path "
-              "(see the sharding notes in DESIGN.md); --gpus must be 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: it measures the single-GPU decode path, "
+              "so --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
