@@ -69,6 +69,25 @@ __device__ inline int page_worker(int64_t ck, int64_t pages, int64_t j, int64_t 
   return (int)(((ck * pages + j * (kPlanOverhead + pages)) * W) / (total * pages));
 }
 
+// First (item, page) of worker w: the first page whose start position is >= w C / Weff, or
+// (n, 0) past the active workers. `cost` holds the cost prefixes of the sorted keys `keys`.
+__device__ inline void worker_start(int64_t w, int n, int64_t Weff, int64_t C, const int* cost, const uint32_t* keys,
+                                    int* sk, int* sp) {
+  if (w >= Weff) { *sk = n; *sp = 0; return; }
+  const int64_t b = w * C;   // position w C / Weff, times Weff
+  int l = 0, r = n - 1;      // largest k with cost[k] Weff <= b
+  while (l < r) {
+    const int m = (l + r + 1) >> 1;
+    if ((int64_t)cost[m] * Weff <= b) l = m; else r = m - 1;
+  }
+  const int64_t pages = 0xFFFF - (int64_t)(keys[l] >> 16);
+  const int64_t num = (b - (int64_t)cost[l] * Weff) * pages;
+  const int64_t den = Weff * (kPlanOverhead + pages);
+  const int64_t j = (num + den - 1) / den;   // smallest j whose start is >= w C / Weff
+  *sk = j < pages ? l : l + 1;
+  *sp = j < pages ? (int)j : 0;
+}
+
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restrict__ seqlens, int batch, int s_q,
                                                          int heads, int causal, int W, int32_t* __restrict__ plan) {
   extern __shared__ __attribute__((aligned(16))) uint32_t sm[];
@@ -93,11 +112,16 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     int sq0, tl0, vis0;
     item_shape(seqlens, 0, tiles, s_q, heads, causal, &sq0, &tl0, &vis0, &first_pages);
   }
+  // Batches of at most one item per thread keep each item's visible length in the upper
+  // half of keys_b (free in both of their paths), so the items pass reads no seqlens again.
+  const bool one_each = n <= nthreads;
+  int* vis_of = reinterpret_cast<int*>(keys_b + kMaxItems / 2);
   bool same = true;
   for (int i = tid; i < n; i += nthreads) {
     int sq, tl, vis, pages;
     item_shape(seqlens, i, tiles, s_q, heads, causal, &sq, &tl, &vis, &pages);
     keys_a[i] = ((uint32_t)(0xFFFF - pages) << 16) | (uint32_t)i;
+    if (one_each) vis_of[i] = vis;
     same = same && pages == first_pages;
   }
   const bool uniform = __syncthreads_and(same);
@@ -196,12 +220,26 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
 
   // owners, splits; slots and split-list positions by one packed scan
   int local_pack = 0;
+  int first1 = 0, ns1 = 0;   // the thread's item when it holds one (one_each)
   for (int k = lo; k < hi; ++k) {
     const int pages = 0xFFFF - (int)(src[k] >> 16);
     const int first = page_worker(cost[k], pages, 0, C, Weff);
     const int last = page_worker(cost[k], pages, pages - 1, C, Weff);
     const int ns = last - first + 1;
     local_pack += ns > 1 ? ((ns << 16) | 1) : 0;
+    first1 = first;
+    ns1 = ns;
+  }
+  // Worker starts, each found once: entry w of `bound` (in the free tail of the cost array)
+  // is worker w's first (item, page) packed as item << 16 | page, read by workers w - 1 and w.
+  int* bound = cost + n;
+  const bool shared_bounds = n + W + 1 <= kMaxItems;
+  if (shared_bounds) {
+    for (int w = tid; w <= W; w += nthreads) {
+      int sk, sp;
+      worker_start(w, n, Weff, C, cost, src, &sk, &sp);
+      bound[w] = (sk << 16) | sp;
+    }
   }
   int pack_total = 0;
   int pack_run = block_exclusive_scan(local_pack, scratch, &pack_total);
@@ -210,11 +248,19 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
   for (int k = lo; k < hi; ++k) {
     const uint32_t key = src[k];
     const int idx = (int)(key & 0xFFFF);
-    int sq, tl, vis, pages;
-    item_shape(seqlens, idx, tiles, s_q, heads, causal, &sq, &tl, &vis, &pages);
-    const int first = page_worker(cost[k], pages, 0, C, Weff);
-    const int last = page_worker(cost[k], pages, pages - 1, C, Weff);
-    const int ns = last - first + 1;
+    int sq, tl, vis, pages, first, ns;
+    if (one_each) {
+      sq = idx / tiles;
+      tl = idx - sq * tiles;
+      vis = vis_of[idx];
+      pages = 0xFFFF - (int)(key >> 16);
+      first = first1;
+      ns = ns1;
+    } else {
+      item_shape(seqlens, idx, tiles, s_q, heads, causal, &sq, &tl, &vis, &pages);
+      first = page_worker(cost[k], pages, 0, C, Weff);
+      ns = page_worker(cost[k], pages, pages - 1, C, Weff) - first + 1;
+    }
     int32_t* it = items + kItemWords * k;
     it[kISeq] = sq;
     it[kITile] = tl;
@@ -235,23 +281,16 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
   }
   // workers: start(w) = the first page whose start position is >= w C / Weff
   int32_t* workers = plan + plan_workers_off(n);
+  if (shared_bounds) __syncthreads();
   for (int w = tid; w < W; w += nthreads) {
     int sk[2], sp[2];
-    for (int e = 0; e < 2; ++e) {
-      const int64_t ww = w + e;
-      if (ww >= Weff) { sk[e] = n; sp[e] = 0; continue; }
-      const int64_t b = ww * C;   // position w C / Weff, times Weff
-      int l = 0, r = n - 1;       // largest k with cost[k] Weff <= b
-      while (l < r) {
-        const int m = (l + r + 1) >> 1;
-        if ((int64_t)cost[m] * Weff <= b) l = m; else r = m - 1;
-      }
-      const int64_t pages = 0xFFFF - (int64_t)(src[l] >> 16);
-      const int64_t num = (b - (int64_t)cost[l] * Weff) * pages;
-      const int64_t den = Weff * (kPlanOverhead + pages);
-      const int64_t j = (num + den - 1) / den;   // smallest j whose start is >= w C / Weff
-      sk[e] = j < pages ? l : l + 1;
-      sp[e] = j < pages ? (int)j : 0;
+    if (shared_bounds) {
+      const int b0 = bound[w], b1 = bound[w + 1];
+      sk[0] = b0 >> 16; sp[0] = b0 & 0xFFFF;
+      sk[1] = b1 >> 16; sp[1] = b1 & 0xFFFF;
+    } else {
+      worker_start(w, n, Weff, C, cost, src, &sk[0], &sp[0]);
+      worker_start(w + 1, n, Weff, C, cost, src, &sk[1], &sp[1]);
     }
     int32_t* wr = workers + kWorkerWords * w;
     wr[0] = sk[0]; wr[1] = sp[0]; wr[2] = sk[1]; wr[3] = sp[1];
