@@ -71,6 +71,8 @@ PLAN_CASES = [
     dict(seqlens=[1000] * 2000, s_q=1, h=128, causal=False, W=256),    # one length, radix-size batch
     dict(seqlens=[500] * 300, s_q=1, h=64, causal=False, W=97),        # one length, 257..1024 items
     dict(seqlens=[700, 700, 64, 700] * 70, s_q=1, h=128, causal=False, W=256),   # 257..1024, mixed
+    dict(seqlens="random16000", s_q=1, h=128, causal=False, W=1024),  # n + W + 1 > 16384: starts not kept in LDS
+    dict(seqlens="random200long", s_q=1, h=128, causal=False, W=4096),  # the most workers, rank sort
 ]
 
 
@@ -81,6 +83,10 @@ def test_device_plan_matches_oracle_definition(case):
         c["seqlens"] = wl._draw_lengths(wl.CONFIGS["jagged"]["lengths"], 128, torch.Generator().manual_seed(1002)).tolist()
     elif c["seqlens"] == "random3000":
         c["seqlens"] = np.random.default_rng(5).integers(0, 20000, 3000).tolist()
+    elif c["seqlens"] == "random16000":
+        c["seqlens"] = np.random.default_rng(9).integers(0, 3000, 16000).tolist()
+    elif c["seqlens"] == "random200long":
+        c["seqlens"] = np.random.default_rng(10).integers(0, 200000, 200).tolist()
     _say("plan case", case, "batch", len(c["seqlens"]))
     sl = torch.tensor(c["seqlens"], dtype=torch.int32, device="cuda")
     plan = mla.get_split_plan(sl, c["s_q"], c["h"], c["causal"], c["W"])
