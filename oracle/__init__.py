@@ -19,6 +19,7 @@ Modules:
            chunks), used to check the device planner bit for bit.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
-(library cross-checks, closed forms, brute force, invariants, printed values);
-none is "parity unpinned".
+(library cross-checks, closed forms, brute force, invariants, printed values, and
+for the cost models an independent tensor inventory), and each pin group has a
+planted-mistake test that must fail it. No function is "parity unpinned".
 """

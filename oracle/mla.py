@@ -36,7 +36,7 @@ Everything is float64; no blocking, fusion or reordering beyond the definition.
 from __future__ import annotations
 
 import math
-from typing import Iterable, List, Optional, Sequence, Tuple
+from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -73,6 +73,11 @@ def e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
     return v
 
 
+# The decoder above applied once to each of the 256 codes: a code's value is a pure function of
+# its 8 bits, so gathering from this table is the same definition, evaluated once per code.
+_E4M3FN_VALUES = e4m3fn_to_f64(np.arange(256, dtype=np.uint8))
+
+
 # ----------------------------------------------------------------------------- cache gather
 
 def latent_rows(kv: np.ndarray, kv_scales: Optional[np.ndarray], kv_dtype: str,
@@ -90,7 +95,9 @@ def latent_rows(kv: np.ndarray, kv_scales: Optional[np.ndarray], kv_dtype: str,
     if kv_dtype == "fp8":
         raw = kv[ids].reshape(npages * PAGE, -1)[:t]
         sc = kv_scales[ids].reshape(npages * PAGE, K_LAT // FP8_TILE)[:t].astype(np.float64)
-        lat = e4m3fn_to_f64(raw[:, :K_LAT]) * np.repeat(sc, FP8_TILE, axis=1)
+        # channel c of a token times its tile's scale, tile = c // 128
+        lat = (_E4M3FN_VALUES[raw[:, :K_LAT]].reshape(t, K_LAT // FP8_TILE, FP8_TILE)
+               * sc[:, :, None]).reshape(t, K_LAT)
         rope = bf16_bits_to_f64(np.ascontiguousarray(raw[:, K_LAT:]).view(np.uint16))
         return np.concatenate([lat, rope], axis=1)
     raise ValueError(kv_dtype)
@@ -138,27 +145,6 @@ def decode_latent(q_bits: np.ndarray, kv: np.ndarray, kv_scales: Optional[np.nda
             o, l = softmax_attention(qz, z[:vis], z[:vis, :K_LAT], scale)
             out[i, j] = o
             lse[i, j] = l
-    return out, lse
-
-
-def decode_latent_rows(q_bits, kv, kv_scales, kv_dtype, block_table, seqlens, scale, causal,
-                       picks: Sequence[Tuple[int, int, int]]):
-    """The same definition evaluated only at sampled (sequence, query token, head) triples.
-    Returns out [n, 512] and lse [n]."""
-    out = np.empty((len(picks), K_LAT))
-    lse = np.empty(len(picks))
-    cache = {}
-    s_q = q_bits.shape[1]
-    for n, (i, j, eta) in enumerate(picks):
-        if i not in cache:
-            cache.clear()
-            cache[i] = latent_rows(kv, kv_scales, kv_dtype, block_table[i], int(seqlens[i]))
-        z = cache[i]
-        vis = visible_keys(int(seqlens[i]), s_q, j, causal)
-        qz = bf16_bits_to_f64(q_bits[i, j, eta])[None, :]
-        o, l = softmax_attention(qz, z[:vis], z[:vis, :K_LAT], scale)
-        out[n] = o[0]
-        lse[n] = l[0]
     return out, lse
 
 

@@ -273,6 +273,80 @@ def test_mlavar6_interpolates_between_endpoints():
     assert f0 == pytest.approx(f_lat) and f1 == pytest.approx(f_fa)
 
 
+def _inventory_bytes(tensors, w=2):
+    """Bytes of a list of tensor shapes at w bytes per element, counted by allocating them."""
+    dt = {1: np.uint8, 2: np.float16, 4: np.float32}[w]
+    return float(sum(np.empty(shape, dtype=dt).nbytes for shape in tensors))
+
+
+# Tiny shapes with distinct primes, so that a swapped, dropped or repeated factor in a byte
+# term changes the total.
+_B, _H, _S, _O, _N, _D, _P, _K = 2, 3, 5, 7, 11, 13, 17, 19
+
+
+def _mlavar6_inventory(b, h, s, o, n, d, p, k):
+    """The tensors one MLAvar6+ call moves, from page "Mla Analysis": section "MLAvar6+ Design"
+    (o old tokens as latent Z, n new tokens decompressed as K, V; t = o + n) and the layouts of
+    section "Tensor Shapes": the query parts Q [B,H,S,D], its absorbed form Qc [B,H,S,K] and its
+    rope part QPE [B,H,S,P]; the old latent rows Z [B,o,K]; the rope keys KPE [B,T,P] of all t
+    tokens; the new K and V [B,n,H,D]; the decompressed output [B,H,S,D] and the latent output
+    [B,H,S,K] that the old part produces before its decompression."""
+    t = o + n
+    return [(b, h, s, d), (b, h, s, k), (b, h, s, p),     # Q, Qc, QPE
+            (b, o, k), (b, t, p),                        # Z (old), KPE (all)
+            (b, n, h, d), (b, n, h, d),                  # K, V (new)
+            (b, h, s, d), (b, h, s, k)]                  # output, latent output
+
+
+def test_mlavar6_bytes_match_tensor_inventory():
+    """Section "Cost Models", MLAvar6+: the byte model equals the bytes of the tensors the split
+    variant reads and writes, counted from arrays of those shapes."""
+    for (o, n) in [(_O, _N), (0, _N), (_O, 0), (1, 1)]:
+        _, byts = om.mlavar6_cost(_B, _H, _S, o, n, d=_D, p=_P, k=_K)
+        assert byts == _inventory_bytes(_mlavar6_inventory(_B, _H, _S, o, n, _D, _P, _K)), (o, n)
+    # w scales every term
+    _, b4 = om.mlavar6_cost(_B, _H, _S, _O, _N, d=_D, p=_P, k=_K, w=4)
+    assert b4 == _inventory_bytes(_mlavar6_inventory(_B, _H, _S, _O, _N, _D, _P, _K), w=4)
+
+
+def test_flashmla_and_flashattention_bytes_match_tensor_inventory():
+    """Section "Cost Models": FlashMLA moves Qc with its rope part and the latent output
+    ([B,H,S,K+P] in, [B,H,S,K] out) and the latent cache Z, KPE ([B,T,K+P]); FlashAttention
+    moves Q, K, V and O with rope parts, [B,H,S+T,2D+P] in total."""
+    t = _O + _N
+    mla_inv = [(_B, _H, _S, _K + _P), (_B, _H, _S, _K), (_B, t, _K + _P)]
+    assert om.flashmla_cost(_B, _H, _S, t, k=_K, p=_P)[1] == _inventory_bytes(mla_inv)
+    fa_inv = [(_B, _H, _S + t, 2 * _D + _P)]
+    assert om.flashattention_cost(_B, _H, _S, t, d=_D, p=_P)[1] == _inventory_bytes(fa_inv)
+
+
+def test_inventory_pin_catches_a_dropped_byte_term(monkeypatch):
+    """A planted mistake in the MLAvar6+ byte model (the second new-token term dropped) fails
+    the inventory pin."""
+    real = om.mlavar6_cost
+
+    def dropped(b, h, s, o, n, d=128, p=64, k=512, w=2):
+        f, by = real(b, h, s, o, n, d=d, p=p, k=k, w=w)
+        return f, by - w * b * h * n * d
+
+    _mutant(monkeypatch, "mlavar6_cost", dropped)
+    with pytest.raises(AssertionError):
+        test_mlavar6_bytes_match_tensor_inventory()
+
+
+def test_inventory_pin_catches_a_transposed_byte_term(monkeypatch):
+    """bok written as bhk (the latent rows counted per head) fails the inventory pin."""
+    real = om.mlavar6_cost
+
+    def transposed(b, h, s, o, n, d=128, p=64, k=512, w=2):
+        f, by = real(b, h, s, o, n, d=d, p=p, k=k, w=w)
+        return f, by - w * b * o * k + w * b * h * k
+
+    _mutant(monkeypatch, "mlavar6_cost", transposed)
+    with pytest.raises(AssertionError):
+        test_mlavar6_bytes_match_tensor_inventory()
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 def _mutant(monkeypatch, name, fn):
