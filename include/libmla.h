@@ -31,8 +31,12 @@
  *    holding tokens 64r .. 64r+63 of sequence i.
  *  - Device-resident preconditions the library cannot check on the host:
  *    0 <= seqlens[i] <= max_pages * 64 and block_table[i, r] in [0, num_pages) for
- *    r < ceil(seqlens[i] / 64). A page id outside [0, num_pages) reads as zeros
- *    (never faults); a length above max_pages * 64 reads only max_pages pages.
+ *    r < ceil(seqlens[i] / 64), and a plan built for the call's arguments. The kernels never
+ *    fault on a violation: a page id outside [0, num_pages) reads as zeros, a length above
+ *    max_pages * 64 reads only max_pages pages, and a mismatched plan writes no output. Each
+ *    violation sets a bit (MLA_DEVICE_*) in the call's optional device status word, and with
+ *    the environment variable MLA_VALIDATE=1 the call synchronises its stream after the launch
+ *    and returns MLA_ERR_INVALID_ARG naming the violations (not under stream capture).
  */
 #ifndef LIBMLA_H
 #define LIBMLA_H
@@ -44,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 /* Status codes returned by every entry point that can fail. */
 typedef enum {
@@ -55,6 +59,12 @@ typedef enum {
   MLA_ERR_HIP = 4,                  /* a HIP runtime call or kernel launch failed */
   MLA_ERR_INTERNAL = 5
 } mla_status;
+
+/* Bits of the device status word (int32, caller-owned device memory, OR-ed by the kernels and
+ * never cleared by them: the caller zeroes it before the calls it wants to watch). */
+#define MLA_DEVICE_PLAN_MISMATCH 1       /* plan built for other batch/s_q/heads/causal/num_workers */
+#define MLA_DEVICE_PAGE_OUT_OF_RANGE 2   /* a needed block-table entry outside [0, num_pages) */
+#define MLA_DEVICE_LENGTH_OVER_CAPACITY 4 /* a sequence length above max_pages * 64 */
 
 /* Storage of the latent cache.
  * MLA_KV_BF16: kv_cache is bf16 [num_pages, 64, 576], a token row = 512 c_KV then 64 rope.
@@ -136,6 +146,10 @@ int32_t mla_get_split_plan(const int32_t* seqlens, int32_t batch, int32_t s_q, i
  *             contents on entry are ignored, on return undefined.
  * out         device float32 [batch, s_q, heads, 512] (normalised O_latent), 16-byte aligned.
  * lse         device float32 [batch, s_q, heads] (natural-log log-sum-exp).
+ * status      device int32 word or NULL: MLA_DEVICE_* bits of violated device-resident
+ *             preconditions are OR-ed into it (see the header comment). 4-byte aligned.
+ * Split sequences: the parts of a sequence cut across workers are merged by log-sum-exp in a
+ * second kernel on the same stream.
  * Calls that overlap on the same workspace race. Results for a fixed plan are bitwise
  * reproducible.
  * Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP. */
@@ -143,7 +157,8 @@ int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scal
                        int64_t num_pages, const int32_t* block_table, int32_t max_pages,
                        const int32_t* seqlens, int32_t batch, int32_t s_q, int32_t heads,
                        float softmax_scale, int32_t causal, const void* plan, int32_t num_workers,
-                       void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream);
+                       void* workspace, size_t workspace_bytes, float* out, float* lse, int32_t* status,
+                       void* stream);
 
 /* Query absorption (page "Mla Analysis", section "Absorption Trick (FlashMLA)": scoring the
  * absorbed query against a latent row equals scoring the query against the decompressed
@@ -208,23 +223,27 @@ size_t mla_sparse_rows_bytes(int32_t batch, int32_t s_q, int32_t topk);
  *             indices, block table and lengths.
  * plan        device buffer of >= mla_plan_bytes(batch * s_q, 1, 128, num_workers) bytes, 16-byte
  *             aligned; written by the device.
+ * status      device int32 word or NULL (MLA_DEVICE_PAGE_OUT_OF_RANGE for a listed key whose
+ *             block-table entry is outside [0, num_pages); that key reads as zeros).
  * Runs entirely on the device. Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
  * MLA_ERR_WORKSPACE_TOO_SMALL (rows_bytes or plan_bytes), MLA_ERR_HIP. */
 int32_t mla_get_sparse_plan(const int32_t* indices, int32_t topk, const int32_t* block_table, int32_t max_pages,
                             const int32_t* seqlens, int32_t batch, int32_t s_q, int32_t heads, int64_t num_pages,
                             int32_t num_workers, void* rows, size_t rows_bytes, void* plan, size_t plan_bytes,
-                            void* stream);
+                            int32_t* status, void* stream);
 
 /* q, out, lse as for mla_decode_fwd ([batch, s_q, 128, ...]). kv_cache, kv_scales: the fp8 cache
  * (kv_dtype must be MLA_KV_FP8_E4M3; a bf16 cache is MLA_ERR_UNSUPPORTED here). rows, plan: from
  * mla_get_sparse_plan with the same batch, s_q, heads, topk, num_pages and num_workers.
  * workspace: >= mla_workspace_bytes(batch * s_q, 1, 128, num_workers) bytes (or NULL when that is
- * 0), 16-byte aligned. Results for a fixed plan are bitwise reproducible.
+ * 0), 16-byte aligned. status: as for mla_decode_fwd. Results for a fixed plan are bitwise
+ * reproducible.
  * Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP. */
 int32_t mla_sparse_decode_fwd(const void* q, const void* kv_cache, const float* kv_scales, int32_t kv_dtype,
                               int64_t num_pages, int32_t batch, int32_t s_q, int32_t heads, int32_t topk,
                               float softmax_scale, const void* rows, const void* plan, int32_t num_workers,
-                              void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream);
+                              void* workspace, size_t workspace_bytes, float* out, float* lse, int32_t* status,
+                              void* stream);
 
 /* Split latent + decompressed attention (page "Mla Analysis", section "MLAvar6+ Design"): a
  * sequence's t cached tokens are split into o old tokens kept as latent rows and its n newest

@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
     L.mla_get_split_plan.argtypes = [c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_p, c_sz, c_p]
     L.mla_decode_fwd.restype = c_i32
     L.mla_decode_fwd.argtypes = [c_p, c_p, c_p, c_i32, c_i64, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_f, c_i32,
-                                 c_p, c_i32, c_p, c_sz, c_p, c_p, c_p]
+                                 c_p, c_i32, c_p, c_sz, c_p, c_p, c_p, c_p]
     L.mla_absorb_query.restype = c_i32
     L.mla_absorb_query.argtypes = [c_p, c_p, c_p, c_i32, c_i32, c_p, c_p]
     L.mla_decompress_output.restype = c_i32
@@ -70,10 +70,10 @@ def lib() -> ctypes.CDLL:
     L.mla_sparse_rows_bytes.argtypes = [c_i32, c_i32, c_i32]
     L.mla_get_sparse_plan.restype = c_i32
     L.mla_get_sparse_plan.argtypes = [c_p, c_i32, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i64, c_i32, c_p, c_sz,
-                                      c_p, c_sz, c_p]
+                                      c_p, c_sz, c_p, c_p]
     L.mla_sparse_decode_fwd.restype = c_i32
     L.mla_sparse_decode_fwd.argtypes = [c_p, c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_f, c_p, c_p,
-                                        c_i32, c_p, c_sz, c_p, c_p, c_p]
+                                        c_i32, c_p, c_sz, c_p, c_p, c_p, c_p]
     L.mla_hybrid_merge.restype = c_i32
     L.mla_hybrid_merge.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_f, c_i32, c_p,
                                    c_p, c_p]
@@ -144,54 +144,88 @@ def get_split_plan(seqlens: torch.Tensor, s_q: int, heads: int, causal: bool = F
     return SplitPlan(buf, batch, s_q, heads, bool(causal), W)
 
 
+def _need(t: torch.Tensor, name: str, dtype, shape, device=None):
+    if (t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)) or not t.is_cuda or not t.is_contiguous()
+            or tuple(t.shape) != tuple(shape) or (device is not None and t.device != device)):
+        raise ValueError(f"{name} must be a contiguous CUDA {dtype} tensor of shape {tuple(shape)}"
+                         + ("" if device is None else f" on {device}"))
+
+
+def _need_bytes(t: torch.Tensor, name: str, nbytes: int, device):
+    if not t.is_cuda or not t.is_contiguous() or t.device != device or t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} must be a contiguous CUDA tensor of at least {nbytes} bytes on {device}")
+
+
+def _status_ptr(status: Optional[torch.Tensor], device):
+    if status is None:
+        return None
+    if status.dtype != torch.int32 or not status.is_cuda or status.numel() < 1 or status.device != device:
+        raise ValueError(f"status must be an int32 CUDA tensor on {device} (its first element is the status word)")
+    return status.data_ptr()
+
+
 def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor,
                softmax_scale: float, kv_scales: Optional[torch.Tensor] = None, causal: bool = False,
                plan: Optional[SplitPlan] = None, workspace: Optional[torch.Tensor] = None,
-               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
-               ) -> Tuple[torch.Tensor, torch.Tensor]:
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               status: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Latent-space MLA decode (see mla_decode_fwd). q: bf16 [b, s, h, 576]; kv_cache: bf16
     [pages, 64, 576] or uint8 [pages, 64, 640] with kv_scales float32 [pages, 64, 4];
     block_table int32 [b, max_pages]; seqlens int32 [b]. Returns out float32 [b, s, h, 512]
-    and lse float32 [b, s, h]."""
-    if q.dim() != 4:
+    and lse float32 [b, s, h]. `status`, an int32 CUDA tensor, receives the device-side
+    MLA_DEVICE_* bits in its first element (OR-ed, never cleared)."""
+    if q.dim() != 4 or q.shape[-1] != 576:
         raise ValueError("q must be [batch, s_q, heads, 576]")
-    batch, s_q, heads, _ = q.shape
+    batch, s_q, heads, _ = (int(x) for x in q.shape)
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (batch, s_q, heads, 576))
+    if kv_cache.dim() != 3:
+        raise ValueError("kv_cache must be [pages, 64, 576] (bf16) or [pages, 64, 640] (fp8 layout)")
+    pages = int(kv_cache.shape[0])
     if kv_cache.dtype == torch.bfloat16:
         kv_dtype = KV_BF16
+        _need(kv_cache, "kv_cache", torch.bfloat16, (pages, 64, 576), dev)
+        if kv_scales is not None:
+            raise ValueError("kv_scales must be None for a bf16 cache")
     elif kv_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
         kv_dtype = KV_FP8_E4M3
+        _need(kv_cache, "kv_cache", (torch.uint8, torch.float8_e4m3fn), (pages, 64, 640), dev)
+        if kv_scales is None:
+            raise ValueError("kv_scales float32 [pages, 64, 4] is required for the fp8 layout")
+        _need(kv_scales, "kv_scales", torch.float32, (pages, 64, 4), dev)
     else:
         raise ValueError("kv_cache must be bfloat16, or uint8/float8_e4m3fn for the fp8 layout")
-    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table), ("seqlens", seqlens)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous CUDA tensor")
-    if q.dtype != torch.bfloat16 or block_table.dtype != torch.int32 or seqlens.dtype != torch.int32:
-        raise ValueError("q must be bfloat16; block_table and seqlens int32")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [batch, max_pages]")
+    _need(block_table, "block_table", torch.int32, (batch, int(block_table.shape[1])), dev)
+    _need(seqlens, "seqlens", torch.int32, (batch,), dev)
     if plan is None:
         plan = get_split_plan(seqlens, s_q, heads, causal)
     if (plan.batch, plan.s_q, plan.heads, plan.causal) != (batch, s_q, heads, bool(causal)):
         raise ValueError("plan was built for different arguments")
     W = plan.num_workers
+    _need_bytes(plan.buffer, "plan buffer", plan_bytes(batch, s_q, heads, W), dev)
     need = workspace_bytes(batch, s_q, heads, W)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need_bytes(workspace, "workspace", need, dev)
     if out is None:
-        out = torch.empty(batch, s_q, heads, 512, dtype=torch.float32, device=q.device)
+        out = torch.empty(batch, s_q, heads, 512, dtype=torch.float32, device=dev)
     if lse is None:
-        lse = torch.empty(batch, s_q, heads, dtype=torch.float32, device=q.device)
-    status = lib().mla_decode_fwd(
+        lse = torch.empty(batch, s_q, heads, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (batch, s_q, heads, 512), dev)
+    _need(lse, "lse", torch.float32, (batch, s_q, heads), dev)
+    status_ptr = _status_ptr(status, dev)
+    rc = lib().mla_decode_fwd(
         q.data_ptr(), kv_cache.data_ptr(), None if kv_scales is None else kv_scales.data_ptr(), kv_dtype,
-        kv_cache.shape[0], block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(), batch, s_q, heads,
+        pages, block_table.data_ptr(), int(block_table.shape[1]), seqlens.data_ptr(), batch, s_q, heads,
         float(softmax_scale), int(causal), plan.buffer.data_ptr(), W,
-        None if workspace is None else workspace.data_ptr(), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-        out.data_ptr(), lse.data_ptr(), _stream(q))
-    _check(int(status))
+        None if workspace is None else workspace.data_ptr(),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        out.data_ptr(), lse.data_ptr(), status_ptr, _stream(q))
+    _check(int(rc))
     return out, lse
-
-
-def _need(t: torch.Tensor, name: str, dtype, shape):
-    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must be a contiguous CUDA {dtype} tensor of shape {tuple(shape)}")
 
 
 def absorb_query(q_nope: torch.Tensor, q_rope: torch.Tensor, w_k: torch.Tensor,
@@ -274,15 +308,18 @@ class SparsePlan:
 
 
 def get_sparse_plan(indices: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor, num_pages: int,
-                    heads: int = 128, num_workers: Optional[int] = None) -> SparsePlan:
+                    heads: int = 128, num_workers: Optional[int] = None,
+                    status: Optional[torch.Tensor] = None) -> SparsePlan:
     """indices int32 [b, s, topk] (logical token positions; entries outside [0, t) are padding),
     block_table int32 [b, max_pages], seqlens int32 [b]."""
     if indices.dim() != 3 or indices.dtype != torch.int32 or not indices.is_cuda or not indices.is_contiguous():
         raise ValueError("indices must be a contiguous CUDA int32 tensor [batch, s_q, topk]")
     b, s_q, topk = (int(x) for x in indices.shape)
-    for name, t in (("block_table", block_table), ("seqlens", seqlens)):
-        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous CUDA int32 tensor")
+    dev = indices.device
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [batch, max_pages]")
+    _need(block_table, "block_table", torch.int32, (b, int(block_table.shape[1])), dev)
+    _need(seqlens, "seqlens", torch.int32, (b,), dev)
     W = default_num_workers(indices.device.index or 0) if num_workers is None else int(num_workers)
     rb = int(lib().mla_sparse_rows_bytes(b, s_q, topk))
     pb = plan_bytes(b * s_q, 1, heads, W)
@@ -292,32 +329,39 @@ def get_sparse_plan(indices: torch.Tensor, block_table: torch.Tensor, seqlens: t
     plan = torch.empty(pb, dtype=torch.uint8, device=indices.device)
     _check(int(lib().mla_get_sparse_plan(indices.data_ptr(), topk, block_table.data_ptr(), int(block_table.shape[1]),
                                          seqlens.data_ptr(), b, s_q, heads, int(num_pages), W, rows.data_ptr(), rb,
-                                         plan.data_ptr(), pb, _stream(indices))))
+                                         plan.data_ptr(), pb, _status_ptr(status, dev), _stream(indices))))
     return SparsePlan(rows, plan, b, s_q, heads, topk, int(num_pages), W)
 
 
 def sparse_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, kv_scales: torch.Tensor, softmax_scale: float,
                       plan: SparsePlan, workspace: Optional[torch.Tensor] = None,
-                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      status: Optional[torch.Tensor] = None):
     """Token-sparse decode over an fp8 cache (see mla_sparse_decode_fwd). q bf16 [b, s, 128, 576];
     kv_cache uint8 [pages, 64, 640]; kv_scales float32 [pages, 64, 4]. Returns out float32
     [b, s, 128, 512] and lse float32 [b, s, 128]."""
     b, s_q, heads = plan.batch, plan.s_q, plan.heads
+    dev = q.device
     _need(q, "q", torch.bfloat16, (b, s_q, heads, 576))
-    if kv_cache.dtype not in (torch.uint8, torch.float8_e4m3fn) or int(kv_cache.shape[0]) != plan.num_pages:
-        raise ValueError("kv_cache must be the fp8 layout [num_pages, 64, 640] the plan was built for")
+    _need(kv_cache, "kv_cache (the fp8 layout the plan was built for)", (torch.uint8, torch.float8_e4m3fn),
+          (plan.num_pages, 64, 640), dev)
+    _need(kv_scales, "kv_scales", torch.float32, (plan.num_pages, 64, 4), dev)
     W = plan.num_workers
     need = workspace_bytes(b * s_q, 1, heads, W)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need_bytes(workspace, "workspace", need, dev)
     if out is None:
-        out = torch.empty(b, s_q, heads, 512, dtype=torch.float32, device=q.device)
+        out = torch.empty(b, s_q, heads, 512, dtype=torch.float32, device=dev)
     if lse is None:
-        lse = torch.empty(b, s_q, heads, dtype=torch.float32, device=q.device)
+        lse = torch.empty(b, s_q, heads, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (b, s_q, heads, 512), dev)
+    _need(lse, "lse", torch.float32, (b, s_q, heads), dev)
     _check(int(lib().mla_sparse_decode_fwd(
         q.data_ptr(), kv_cache.data_ptr(), kv_scales.data_ptr(), KV_FP8_E4M3, plan.num_pages, b, s_q, heads, plan.topk,
         float(softmax_scale), plan.rows.data_ptr(), plan.plan.data_ptr(), W,
         None if workspace is None else workspace.data_ptr(),
         0 if workspace is None else workspace.numel() * workspace.element_size(), out.data_ptr(), lse.data_ptr(),
-        _stream(q))))
+        _status_ptr(status, dev), _stream(q))))
     return out, lse

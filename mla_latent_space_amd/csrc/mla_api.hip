@@ -4,12 +4,20 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <string>
 
 #include "libmla.h"
 #include "mla_internal.h"
 
+// Library-owned device word (one copy per GPU, alive until the process ends): the status word
+// of calls validated without a caller status word.
+static __device__ int32_t g_validate_status;
+
 namespace {
+
+__global__ void clear_word_kernel(int32_t* w) { *w = 0; }
 
 thread_local char g_err[512] = "";
 
@@ -27,6 +35,52 @@ int32_t ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool env_flag(const char* name) {
+  const char* e = std::getenv(name);
+  return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+}
+
+std::string describe_status(int32_t bits) {
+  std::string m;
+  auto add = [&](int32_t b, const char* what) {
+    if (bits & b) m += std::string(m.empty() ? "" : "; ") + what;
+  };
+  add(mla::kDevPlanMismatch, "the plan was built for other arguments (batch, s_q, heads, causal or num_workers)");
+  add(mla::kDevPageOutOfRange, "a block-table entry a sequence needs is outside [0, num_pages)");
+  add(mla::kDevLengthOverCap, "a sequence length exceeds max_pages * 64");
+  return m;
+}
+
+// MLA_VALIDATE=1: the device status word of the call (the caller's, or the library's own
+// word cleared first) is read after a stream synchronisation, and any bit set turns the call
+// into MLA_ERR_INVALID_ARG. Returns the status pointer the kernels should use.
+int32_t* validate_begin(int32_t* status, hipStream_t stream, bool* on) {
+  *on = false;
+  if (!env_flag("MLA_VALIDATE")) return status;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return status;
+  *on = true;
+  if (status != nullptr) return status;
+  int32_t* w = nullptr;
+  if (hipGetSymbolAddress(reinterpret_cast<void**>(&w), HIP_SYMBOL(g_validate_status)) != hipSuccess) {
+    *on = false;
+    return nullptr;
+  }
+  hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, stream, w);
+  return w;
+}
+
+int32_t validate_end(int32_t* word, hipStream_t stream, const char* call) {
+  int32_t bits = 0;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMemcpy(&bits, word, sizeof(bits), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: validation read-back: %s", call, hipGetErrorString(e));
+  if (bits != 0)
+    return fail(MLA_ERR_INVALID_ARG, "%s: device-side check failed (status 0x%x): %s", call, (unsigned)bits,
+                describe_status(bits).c_str());
+  return ok();
+}
 
 // Shape checks shared by the plan and the decode call.
 int32_t check_shape(int32_t batch, int32_t s_q, int32_t heads, int32_t causal, int32_t num_workers) {
@@ -123,7 +177,7 @@ int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scal
                        int64_t num_pages, const int32_t* block_table, int32_t max_pages, const int32_t* seqlens,
                        int32_t batch, int32_t s_q, int32_t heads, float softmax_scale, int32_t causal,
                        const void* plan, int32_t num_workers, void* workspace, size_t workspace_bytes, float* out,
-                       float* lse, void* stream) {
+                       float* lse, int32_t* status, void* stream) {
   int32_t st = check_shape(batch, s_q, heads, causal, num_workers);
   if (st != MLA_OK) return st;
   if (!q || !kv_cache || !block_table || !seqlens || !plan || !out || !lse)
@@ -166,10 +220,15 @@ int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scal
   a.out = out;
   a.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (status && (reinterpret_cast<uintptr_t>(status) & 3u))
+    return fail(MLA_ERR_INVALID_ARG, "status must be 4-byte aligned");
+  bool validating = false;
+  a.status = validate_begin(status, s, &validating);
   hipError_t e = mla::launch_decode_rows32(a, kv_dtype == MLA_KV_FP8_E4M3, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
   e = mla::launch_combine_rows32(a, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+  if (validating) return validate_end(a.status, s, "mla_decode_fwd");
   return ok();
 }
 
@@ -234,7 +293,7 @@ static int32_t check_sparse(int32_t batch, int32_t s_q, int32_t heads, int32_t t
 int32_t mla_get_sparse_plan(const int32_t* indices, int32_t topk, const int32_t* block_table, int32_t max_pages,
                             const int32_t* seqlens, int32_t batch, int32_t s_q, int32_t heads, int64_t num_pages,
                             int32_t num_workers, void* rows, size_t rows_bytes, void* plan, size_t plan_bytes,
-                            void* stream) {
+                            int32_t* status, void* stream) {
   int32_t st = check_sparse(batch, s_q, heads, topk, num_pages, num_workers);
   if (st != MLA_OK) return st;
   if (!indices || !block_table || !seqlens || !rows || !plan)
@@ -254,18 +313,24 @@ int32_t mla_get_sparse_plan(const int32_t* indices, int32_t topk, const int32_t*
   int32_t* rows32 = static_cast<int32_t*>(rows);
   int32_t* vis = rows32 + (int64_t)n * stride;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (status && (reinterpret_cast<uintptr_t>(status) & 3u))
+    return fail(MLA_ERR_INVALID_ARG, "status must be 4-byte aligned");
+  bool validating = false;
+  int32_t* sw = validate_begin(status, s, &validating);
   hipError_t e = mla::launch_sparse_rows(indices, topk, block_table, max_pages, seqlens, batch, s_q, num_pages,
-                                         rows32, stride, vis, s);
+                                         rows32, stride, vis, sw, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "row-list kernel launch: %s", hipGetErrorString(e));
   e = mla::launch_plan(vis, n, 1, heads, 0, num_workers, static_cast<int32_t*>(plan), s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan kernel launch: %s", hipGetErrorString(e));
+  if (validating) return validate_end(sw, s, "mla_get_sparse_plan");
   return ok();
 }
 
 int32_t mla_sparse_decode_fwd(const void* q, const void* kv_cache, const float* kv_scales, int32_t kv_dtype,
                               int64_t num_pages, int32_t batch, int32_t s_q, int32_t heads, int32_t topk,
                               float softmax_scale, const void* rows, const void* plan, int32_t num_workers,
-                              void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream) {
+                              void* workspace, size_t workspace_bytes, float* out, float* lse, int32_t* status,
+                              void* stream) {
   int32_t st = check_sparse(batch, s_q, heads, topk, num_pages, num_workers);
   if (st != MLA_OK) return st;
   if (!q || !kv_cache || !kv_scales || !rows || !plan || !out || !lse)
@@ -303,10 +368,15 @@ int32_t mla_sparse_decode_fwd(const void* q, const void* kv_cache, const float* 
   a.out = out;
   a.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (status && (reinterpret_cast<uintptr_t>(status) & 3u))
+    return fail(MLA_ERR_INVALID_ARG, "status must be 4-byte aligned");
+  bool validating = false;
+  a.status = validate_begin(status, s, &validating);
   hipError_t e = mla::launch_decode_sparse_fp8(a, static_cast<const int32_t*>(rows), stride, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
   e = mla::launch_combine_rows32(a, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+  if (validating) return validate_end(a.status, s, "mla_sparse_decode_fwd");
   return ok();
 }
 

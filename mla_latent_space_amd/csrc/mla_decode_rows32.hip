@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     const __bf16* __restrict__ q_ptr, const char* __restrict__ kv_ptr, const float* __restrict__ kv_scales,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ plan, float* __restrict__ ws,
     float* __restrict__ out_ptr, float* __restrict__ lse_ptr, const int32_t* __restrict__ srows, int srow_stride,
-    Scalars a) {
+    int32_t* __restrict__ status, Scalars a) {
   static_assert(kFp8 || !kSparse, "the token-sparse path reads an fp8 cache");
   constexpr int kPBase = kFp8 ? kR8PBase : kR32PBase;   // P buffers; votes and 1/l after the loop
   constexpr int kLoadSlots = kFp8 ? kR8Stage : kR32Slots;
@@ -251,10 +251,20 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int worker = xcd_worker();
+  // device-side precondition violations of this work-group, reported once at the end
+  int dev_err = 0;
+  auto report = [&]() {
+    if (status != nullptr && dev_err != 0 && threadIdx.x == 0)
+      __hip_atomic_fetch_or(status, dev_err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   if (plan[kHMagic] != kPlanMagic || plan[kHVersion] != kPlanVersion || plan[kHWorkers] != (int)gridDim.x ||
       plan[kHBatch] != a.batch ||
-      plan[kHSq] != a.s_q || plan[kHHeads] != a.heads || plan[kHCausal] != a.causal)
+      plan[kHSq] != a.s_q || plan[kHHeads] != a.heads || plan[kHCausal] != a.causal ||
+      plan[kHItems] != a.batch * tiles_per_seq(a.s_q, a.heads)) {
+    dev_err = kDevPlanMismatch;
+    report();
     return;
+  }
   const int n_items = plan[kHItems];
   const int32_t* wr = plan + plan_workers_off(n_items) + kWorkerWords * worker;
   const int kb = wr[0], pb = wr[1], ke = wr[2], pe = wr[3];
@@ -275,7 +285,6 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   // 16ks + 8(l/32) .. +7. Rows past the last query row (a partial tile) load the sequence's
   // first row: every output column depends on its own row only, and no such row is written.
   bf16x8 qreg[36];
-  int q_item = -1;
   auto load_q = [&](int k) {
     int l = lane;
     asm volatile("" : "+v"(l));
@@ -287,7 +296,6 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     const __bf16* qrow = q_ptr + ((int64_t)(it[kISeq] * a.s_q + jt) * a.heads + hd) * kDqk + 8 * (l >> 5);
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
-    q_item = k;
   };
   // ---- load cursor: the first kR32Slots-1 steps are issued up front, then one step per
   // compute region (its DMA instructions spread between the score MFMAs)
@@ -335,7 +343,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         z.sc = make_rsrc(reinterpret_cast<uint64_t>(kv_scales), (int)(a.num_pages * (kPage * 16)));
         return z;
       } else {
-        return cursor_rsrc<kFp8>(lc, a, kv_ptr, kv_scales);
+        return cursor_rsrc<kFp8>(lc, a, kv_ptr, kv_scales, dev_err);
       }
     }
     z.kv = z.sc = make_rsrc(reinterpret_cast<uint64_t>(kv_ptr), 0);
@@ -512,7 +520,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
   // registers, each load instruction would touch 32 rows; with every worker starting at
   // once, that burst is bound by the number of cache lines.) Rows past the last query row
   // read as zeros. Then the first ring steps.
-  {
+  auto start_up = [&]() {
     const int32_t* it = plan + plan_items_off() + kItemWords * kb;
     const int tile0 = kRowsPerTile * it[kITile];
     const int valid_rows = rows_total - tile0 < kRowsPerTile ? rows_total - tile0 : kRowsPerTile;
@@ -531,15 +539,14 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     const QkAddr qa = qk_at(qk0, (uint32_t)wave * kBufBytes);
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) qreg[ks] = lds_b128(lds + (qa.b[ks & 3] + 128 * (ks >> 2)));
-    q_item = kb;
     barrier_lds();   // every wave holds its rows before the ring is refilled
-  }
-  if constexpr (kFp8) {
-    f8_fill(true);
-  } else {
+    if constexpr (kFp8) {
+      f8_fill(true);
+    } else {
 #pragma unroll 1
-    for (int i = 0; i < kR32Slots - 1; ++i) issue_step();
-  }
+      for (int i = 0; i < kR32Slots - 1; ++i) issue_step();
+    }
+  };
 
   int comp_slot = 0;   // ring slot of the segment's current step
 
@@ -557,6 +564,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     {
       const int tile_row0 = kRowsPerTile * it[kITile];
       const int g_row = tile_row0 + 32 * wave + (lane & 31);
+      if (it[kIVis] > a.max_pages * kPage) dev_err |= kDevLengthOverCap;
       if (g_row < rows_total) {
         const int vis = it[kIVis];
         const int cap = a.max_pages * kPage;
@@ -580,7 +588,13 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       }
       lim_min = __builtin_amdgcn_readfirstlane(m);
     }
-    if (q_item != k) load_q(k);   // (after an item with no steps)
+    // this item's query rows: the first item's staged at start-up (which then issues the first
+    // ring steps), the others loaded into registers (no DMA step is issued between the previous
+    // item's last steps and these loads, so they are the youngest loads in flight and waiting
+    // for them at their first use leaves no ring step behind). Defined on every path here, the
+    // rows of the previous item are dead through its finalize.
+    if (k == kb) start_up();
+    else load_q(k);
     if constexpr (kFp8) {
       // Q^T k-steps 34, 35 of the item to LDS (this wave's area; the score loops read them
       // back there, which frees 8 VGPRs in the step loop)
@@ -974,11 +988,18 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       int l = lane;
       asm volatile("" : "+v"(l));
       const int32_t* itf = plan + plan_items_off() + kItemWords * k;
-      const int f_seq = itf[kISeq], f_tile = itf[kITile];
-      const bool split = itf[kINsplits] > 1;
+      const int f_seq = itf[kISeq], f_tile = itf[kITile], f_ns = itf[kINsplits];
+      const bool split = f_ns > 1;
       const int slot = split ? itf[kISlot] + (worker - itf[kIOwner]) : 0;
       const int row0 = kRowsPerTile * f_tile + 32 * wave;   // the first row this wave owns
       float __attribute__((address_space(3)))* inv_s = (float __attribute__((address_space(3)))*)(lds + kPBase + 64);
+      // out row of register r of a tile of row block rb, and its column base for this lane
+      auto out_row = [&](int rb, int r, bool& ok) -> float* {
+        const int grow = kRowsPerTile * f_tile + 32 * rb + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        ok = grow < rows_total;
+        const int jt = ok ? grow / a.heads : 0, hd = ok ? grow - jt * a.heads : 0;
+        return out_ptr + ((int64_t)(f_seq * a.s_q + jt) * a.heads + hd) * kLat + 128 * wave + (l & 31);
+      };
       if (!split) {
         if (l < 32) inv_s[32 * wave + l] = l_run > 0.f ? 1.f / l_run : 0.f;
         barrier_lds();   // every row's 1/l from the wave that owns it
@@ -993,7 +1014,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
           for (int c = 0; c < 4; ++c) {
             bf16x8 v0, v1;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {   // unnormalised: the combine divides by the denominator
+            for (int r = 0; r < 8; ++r) {   // unnormalised: the merge divides by the denominator
               v0[r] = (__bf16)o[4 * g + c][r];
               v1[r] = (__bf16)o[4 * g + c][8 + r];
             }
@@ -1014,10 +1035,8 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
             inv4[j] = *(const f32x4 __attribute__((address_space(3)))*)(inv_s + 32 * rb + 8 * j + 4 * (l >> 5));
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int grow = kRowsPerTile * f_tile + 32 * rb + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-            const bool ok = grow < rows_total;
-            const int jt = ok ? grow / a.heads : 0, hd = ok ? grow - jt * a.heads : 0;
-            float* dst = out_ptr + ((int64_t)(f_seq * a.s_q + jt) * a.heads + hd) * kLat + 128 * wave + (l & 31);
+            bool ok;
+            float* dst = out_row(rb, r, ok);
             const float sc = inv4[r >> 2][r & 3];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -1047,11 +1066,8 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // the next item's query rows: the youngest loads in flight, so waiting for them (at
-    // their first use) leaves no ring step behind
-    __builtin_amdgcn_sched_barrier(0);
-    if (k < k_last) load_q(k + 1);
   }
+  report();
 }
 
 // Merge the partials of split items written by decode_rows32_kernel. Part k of a row holds
@@ -1070,8 +1086,9 @@ constexpr int kCmbBatch = 4;         // parts whose data is in flight together
 __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32_t* __restrict__ plan,
                                                                      const char* __restrict__ ws,
                                                                      float* __restrict__ out,
-                                                                     float* __restrict__ lse, int s_q, int heads,
-                                                                     int n_items, int workers) {
+                                                                     float* __restrict__ lse, int batch, int s_q,
+                                                                     int heads, int causal, int n_items, int workers,
+                                                                     int32_t* __restrict__ status) {
   __shared__ __attribute__((aligned(16))) float wts[kCmbMaxSplits][32];   // [part][row]: m_k, then weights
   __shared__ float dens[kCmbMaxSplits][32];                               // [part][row]: l_k
   __shared__ float tile_out[32][128 + 4];
@@ -1080,10 +1097,18 @@ __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32
   __shared__ float row_m[32];
   // the header and this block's split record in one round trip (the record area holds
   // n_items entries, so the read is in bounds for every block of the grid)
+  // A plan built for other arguments fails the header check before any record is used.
+  if (plan[kHMagic] != kPlanMagic || plan[kHVersion] != kPlanVersion || plan[kHBatch] != batch ||
+      plan[kHSq] != s_q || plan[kHHeads] != heads || plan[kHCausal] != causal || plan[kHWorkers] != workers ||
+      plan[kHItems] != n_items) {
+    if (status != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+      __hip_atomic_fetch_or(status, (int)kDevPlanMismatch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int n_split = plan[kHSplitItems];
+  if ((int)blockIdx.x >= n_split) return;
   const int32_t* sr = plan + plan_split_off(n_items, workers) + kSplitWords * blockIdx.x;
-  const int magic = plan[kHMagic], n_split = plan[kHSplitItems];
   const int seq = sr[kSSeq], tile = sr[kSTile], ns_all = sr[kSNsplits], slot0 = sr[kSSlot];
-  if (magic != kPlanMagic || (int)blockIdx.x >= n_split) return;
   const int rows_total = s_q * heads;
   const int w = blockIdx.y, cq = blockIdx.z;
   if (kRowsPerTile * tile + 32 * w >= rows_total) return;
@@ -1212,7 +1237,7 @@ hipError_t launch_rows32(const DecodeArgs& a, const int32_t* srows, int srow_str
   }
   hipLaunchKernelGGL((decode_rows32_kernel<kFp8, kSparse>), dim3(a.workers), dim3(kR32Threads), lds_bytes, stream,
                      reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const char*>(a.kv), a.kv_scales,
-                     a.block_table, a.plan, a.ws, a.out, a.lse, srows, srow_stride, scalars_of(a));
+                     a.block_table, a.plan, a.ws, a.out, a.lse, srows, srow_stride, a.status, scalars_of(a));
   return hipGetLastError();
 }
 
@@ -1230,7 +1255,8 @@ hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream) {
   const int n_items = a.batch * tiles_per_seq(a.s_q, a.heads);
   const int max_split = a.workers < n_items ? a.workers : n_items;   // split items <= both
   hipLaunchKernelGGL(combine_rows32_kernel, dim3(max_split, kRowsPerTile / 32, 4), dim3(kCmbThreads), 0, stream,
-                     a.plan, reinterpret_cast<const char*>(a.ws), a.out, a.lse, a.s_q, a.heads, n_items, a.workers);
+                     a.plan, reinterpret_cast<const char*>(a.ws), a.out, a.lse, a.batch, a.s_q, a.heads, a.causal,
+                     n_items, a.workers, a.status);
   return hipGetLastError();
 }
 

@@ -61,25 +61,20 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 // num_records read as zero) into LDS at m0 + 16 * lane. Written as inline asm so that the
 // compiler does not track it as a pending LDS write: it would otherwise wait vmcnt(0)
 // before unrelated LDS reads and drain the prefetch ring. The kernel orders these loads
-// itself with wait_vmcnt + barrier_lds. No register outputs (nothing is left in flight
-// in a VGPR).
+// itself with wait_vmcnt + barrier_lds. The LDS address is an operand bound to m0, so the
+// compiler sets m0 itself and knows it is in use; the instruction has no register outputs
+// (nothing is left in flight in a VGPR).
 __device__ __forceinline__ void lds_dma_x4(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
-      : "m0");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)));
 }
 
 // The same with 64 lanes x 4 B (LDS at m0 + 4 * lane).
 __device__ __forceinline__ void lds_dma_x1(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dword %1, %2, 0 offen lds"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
-      : "m0");
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)));
 }
 
 // Work-group barrier for LDS traffic only. __syncthreads() also orders the LDS-DMA loads
@@ -155,10 +150,14 @@ __device__ __forceinline__ i32x4 make_rsrc(uint64_t addr, int bytes) {
 
 template <bool kFp8>
 __device__ __forceinline__ StepRsrc cursor_rsrc(const LoadCursor& c, const Scalars& a, const char* __restrict__ kv,
-                                                const float* __restrict__ scales) {
+                                                const float* __restrict__ scales, int& dev_err) {
   int valid = c.vis - kStep * c.hh;
   valid = valid > kStep ? kStep : valid;
-  const bool ok = c.pid >= 0 && (int64_t)c.pid < a.num_pages && valid > 0;
+  const bool in_range = c.pid >= 0 && (int64_t)c.pid < a.num_pages;
+  const bool ok = in_range && valid > 0;
+  // a page the step needs whose block-table entry lies outside the cache (entries past
+  // max_pages are a length above capacity, reported on its own)
+  if (valid > 0 && !in_range && (c.hh >> 1) < a.max_pages) dev_err |= kDevPageOutOfRange;
   StepRsrc r;
   if constexpr (!kFp8) {
     const uint64_t addr = reinterpret_cast<uint64_t>(kv) +
@@ -184,14 +183,17 @@ __device__ __forceinline__ bf16x4 lds_tr16(const char __attribute__((address_spa
 }
 
 
-// Work-groups are dealt to the 8 XCDs round-robin (block b -> XCD b % 8). Plan workers are
-// numbered so that consecutive ones (the parts of one split item, which all load the item's
-// queries) share an XCD and its L2: worker = (blocks on lower XCDs) + b / 8.
+// Work-groups are dealt to the 8 XCDs round-robin (consecutive blocks on consecutive XCDs;
+// which XCD block 0 lands on varies between launches). Plan workers are numbered so that
+// consecutive ones (the parts of one split item, which all load the item's queries) are
+// blocks of one residue class and so share an XCD and its L2: worker = (blocks of lower
+// residues) + b / 8. This only places work; nothing relies on it for correctness.
+constexpr int kXcds = 8;
 __device__ __forceinline__ int xcd_worker() {
-  const int b = blockIdx.x, n = gridDim.x, x = b & 7;
+  const int b = blockIdx.x, n = gridDim.x, x = b % kXcds;
   int before = 0;
-  for (int y = 0; y < x; ++y) before += (n - y + 7) >> 3;
-  return before + (b >> 3);
+  for (int y = 0; y < x; ++y) before += (n - y + kXcds - 1) / kXcds;
+  return before + b / kXcds;
 }
 
 }  // namespace

@@ -44,6 +44,13 @@ __host__ __device__ inline int plan_split_off(int n_items, int workers) {
 __host__ __device__ inline int64_t plan_words(int n_items, int workers) {
   return (int64_t)plan_split_off(n_items, workers) + (int64_t)kSplitWords * n_items;
 }
+
+// Device-side precondition violations, OR-ed into the caller's status word (libmla.h).
+enum DeviceStatus {
+  kDevPlanMismatch = 1,      // the plan header does not match the call
+  kDevPageOutOfRange = 2,    // a needed block-table entry is outside [0, num_pages)
+  kDevLengthOverCap = 4,     // a length above max_pages * 64
+};
 __host__ __device__ inline int tiles_per_seq(int s_q, int heads) {
   return (s_q * heads + kRowsPerTile - 1) / kRowsPerTile;
 }
@@ -73,13 +80,14 @@ struct DecodeArgs {
   float* ws;          // partial slots
   float* out;
   float* lse;
+  int32_t* status;    // device status word (may be null)
 };
 
 hipError_t launch_decode_rows32(const DecodeArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_decode_sparse_fp8(const DecodeArgs& a, const int32_t* rows, int row_stride, hipStream_t stream);
 hipError_t launch_sparse_rows(const int32_t* indices, int topk, const int32_t* block_table, int max_pages,
                               const int32_t* seqlens, int batch, int s_q, int64_t num_pages, int32_t* rows,
-                              int stride, int32_t* vis, hipStream_t stream);
+                              int stride, int32_t* vis, int32_t* status, hipStream_t stream);
 // token-sparse decode: row lists [batch * s_q, stride] (stride = topk rounded up to 32), then
 // the visible counts [batch * s_q]
 inline int sparse_stride(int topk) { return (topk + 31) / 32 * 32; }

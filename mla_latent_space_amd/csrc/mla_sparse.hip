@@ -4,7 +4,7 @@
 // turns every list into the cache rows the decode kernel gathers: entry u of the list is a key
 // when 0 <= u < min(t_i, max_pages * 64) (others are padding and dropped), its row is
 // block_table[i, u / 64] * 64 + u % 64, stored + 1 (0 = a key whose page id is outside
-// [0, num_pages), which reads as zeros, as in the dense decode). The kept entries are packed
+// [0, num_pages), which reads as zeros, as in the dense decode, and is reported in the status word). The kept entries are packed
 // to the front of the query token's row list, in list order, the rest filled with 0, and their
 // count becomes that query token's visible length for the split plan, which then treats each
 // query token as a sequence of one query row per head.
@@ -26,7 +26,8 @@ __global__ __launch_bounds__(kSrThreads) void sparse_rows_kernel(const int32_t* 
                                                                  const int32_t* __restrict__ block_table,
                                                                  int max_pages, const int32_t* __restrict__ seqlens,
                                                                  int s_q, int64_t num_pages, int32_t* __restrict__ rows,
-                                                                 int stride, int32_t* __restrict__ vis) {
+                                                                 int stride, int32_t* __restrict__ vis,
+                                                                 int32_t* __restrict__ status) {
   __shared__ int wave_tot[4];
   const int v = blockIdx.x, i = v / s_q, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int t = seqlens[i];
@@ -35,6 +36,7 @@ __global__ __launch_bounds__(kSrThreads) void sparse_rows_kernel(const int32_t* 
   const int32_t* src = indices + (int64_t)v * topk;
   int32_t* dst = rows + (int64_t)v * stride;
   int kept = 0;   // keys placed by the earlier blocks (the same in every thread)
+  bool bad_page = false;
   for (int e0 = 0; e0 < topk; e0 += kSrThreads * kSrPer) {
     int u[kSrPer], stored[kSrPer];
 #pragma unroll
@@ -49,7 +51,9 @@ __global__ __launch_bounds__(kSrThreads) void sparse_rows_kernel(const int32_t* 
       stored[r] = -1;   // (not a key)
       if (key) {
         const int pid = block_table[(int64_t)i * max_pages + (u[r] >> 6)];
-        stored[r] = (pid >= 0 && (int64_t)pid < num_pages) ? pid * kPage + (u[r] & (kPage - 1)) + 1 : 0;
+        const bool in_range = pid >= 0 && (int64_t)pid < num_pages;
+        stored[r] = in_range ? pid * kPage + (u[r] & (kPage - 1)) + 1 : 0;
+        bad_page = bad_page || !in_range;
         ++mine;
       }
     }
@@ -74,15 +78,17 @@ __global__ __launch_bounds__(kSrThreads) void sparse_rows_kernel(const int32_t* 
   }
   for (int e = kept + tid; e < stride; e += kSrThreads) dst[e] = 0;
   if (tid == 0) vis[v] = kept;
+  if (status != nullptr && bad_page)
+    __hip_atomic_fetch_or(status, (int)kDevPageOutOfRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
 hipError_t launch_sparse_rows(const int32_t* indices, int topk, const int32_t* block_table, int max_pages,
                               const int32_t* seqlens, int batch, int s_q, int64_t num_pages, int32_t* rows,
-                              int stride, int32_t* vis, hipStream_t stream) {
+                              int stride, int32_t* vis, int32_t* status, hipStream_t stream) {
   hipLaunchKernelGGL(sparse_rows_kernel, dim3(batch * s_q), dim3(kSrThreads), 0, stream, indices, topk, block_table,
-                     max_pages, seqlens, s_q, num_pages, rows, stride, vis);
+                     max_pages, seqlens, s_q, num_pages, rows, stride, vis, status);
   return hipGetLastError();
 }
 

@@ -40,12 +40,20 @@ class Dev:
     def plan(self, num_workers=None):
         return mla.get_split_plan(self.sl, self.w.s_q, self.w.heads, self.w.causal, num_workers)
 
-    def run(self, num_workers=None, plan=None):
+    def run(self, num_workers=None, plan=None, expect_status=0):
+        """One decode call. out and lse start as NaN, so an output the kernels never write
+        cannot pass on stale memory; the device status word must read `expect_status`."""
         if plan is None:
             plan = self.plan(num_workers)
-        out, lse = mla.decode_fwd(self.q, self.kv, self.bt, self.sl, self.w.scale, kv_scales=self.scales,
-                                  causal=self.w.causal, plan=plan)
+        w = self.w
+        out = torch.full((w.batch, w.s_q, w.heads, 512), float("nan"), dtype=torch.float32, device=self.q.device)
+        lse = torch.full((w.batch, w.s_q, w.heads), float("nan"), dtype=torch.float32, device=self.q.device)
+        status = torch.zeros(1, dtype=torch.int32, device=self.q.device)
+        mla.decode_fwd(self.q, self.kv, self.bt, self.sl, w.scale, kv_scales=self.scales, causal=w.causal, plan=plan,
+                       out=out, lse=lse, status=status)
         torch.cuda.synchronize()
+        got = int(status.item())
+        assert got == expect_status, f"device status word {got:#x}, expected {expect_status:#x}"
         return out, lse
 
 

@@ -1,5 +1,6 @@
 """The C ABI library loads, exports every declared entry point, and rejects bad arguments on
-the host before any HIP call (CPU only: no compute is launched)."""
+the host before any HIP call (CPU only: no compute is launched). The library must have been
+built (``__graft_entry__.build()``): a missing libmla.so fails these tests."""
 import ctypes
 import os
 import re
@@ -11,7 +12,9 @@ import mla_latent_space_amd as mla
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "libmla.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(mla.LIB_PATH), reason="libmla.so not built")
+
+def test_library_is_built():
+    assert os.path.exists(mla.LIB_PATH), f"{mla.LIB_PATH} is missing: run __graft_entry__.build() first"
 
 
 def declared_functions():
@@ -32,14 +35,15 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = mla.lib()
-    assert mla.abi_version() == 1
+    assert mla.abi_version() == 2
     assert L.mla_status_string(0) == b"MLA_OK"
     assert L.mla_status_string(3) == b"MLA_ERR_WORKSPACE_TOO_SMALL"
     assert L.mla_status_string(99) == b"unknown status"
 
 
 def test_sizes():
-    # 64 items (one 128-row tile each), 256 workers
+    # 64 items (one 128-row tile each), 256 workers: header, items (8 words), workers (4),
+    # split records (4 per item)
     n, W = 64, 256
     assert mla.plan_bytes(64, 1, 128, W) == 4 * (16 + 8 * n + 4 * W + 4 * n)
     assert mla.plan_bytes(32, 16, 128, W) == 4 * (16 + 12 * 32 * 16 + 4 * W)
@@ -76,7 +80,7 @@ def _decode(L, **kw):
     a.update(kw)
     return L.mla_decode_fwd(a["q"], a["kv"], a["scales"], a["dtype"], a["num_pages"], a["bt"], a["max_pages"], a["sl"],
                             a["batch"], a["s_q"], a["h"], a["scale"], a["causal"], a["plan"], a["W"], a["ws"],
-                            a["ws_bytes"], a["out"], a["lse"], None)
+                            a["ws_bytes"], a["out"], a["lse"], a.get("status"), None)
 
 
 def test_decode_rejects_bad_arguments_before_launch():
@@ -99,6 +103,8 @@ def test_decode_rejects_bad_arguments_before_launch():
     assert _decode(L, ws=None) == 3
     assert _decode(L, out=ctypes.c_void_p(0x100008)) == 1  # misaligned
     assert b"16-byte aligned" in L.mla_last_error_message()
+    assert _decode(L, status=ctypes.c_void_p(0x100002)) == 1   # a status word must be 4-byte aligned
+    assert b"status" in L.mla_last_error_message()
 
 
 def test_projections_reject_bad_arguments_before_launch():
@@ -153,7 +159,7 @@ def test_sparse_calls_reject_bad_arguments_before_launch():
     def plan(indices=f, topk=64, max_pages=8, batch=2, s_q=1, heads=128, pages=100, W=8, rows_bytes=1 << 20,
              plan_bytes=1 << 20, rows=f):
         return L.mla_get_sparse_plan(indices, topk, f, max_pages, f, batch, s_q, heads, pages, W, rows, rows_bytes, f,
-                                     plan_bytes, None)
+                                     plan_bytes, None, None)
 
     assert plan(indices=None) == 1
     assert plan(topk=0) == 1 and plan(batch=0) == 1 and plan(pages=0) == 1 and plan(max_pages=0) == 1
@@ -165,7 +171,7 @@ def test_sparse_calls_reject_bad_arguments_before_launch():
 
     def dec(kv_dtype=1, q=f, scales=f, heads=128, scale=0.1, ws_bytes=1 << 30, out=f):
         return L.mla_sparse_decode_fwd(q, f, scales, kv_dtype, 100, 2, 1, heads, 64, scale, f, f, 8, f, ws_bytes, out,
-                                       f, None)
+                                       f, None, None)
 
     assert dec(kv_dtype=0) == 2                         # bf16 cache: not on this path
     assert dec(kv_dtype=7) == 1

@@ -1,6 +1,6 @@
 """GPU parity: the HIP library (through the C ABI) against the fp64 oracle on the same seeded
-inputs. Small cases compare every output element; full-size workloads compare every row of
-sampled sequences. The split plan must match the oracle's plan definition bit for bit."""
+inputs. Every case compares every output element, the full-size workloads included (two seeds
+each). The split plan must match the oracle's plan definition bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -34,16 +34,6 @@ def _check_full(w, num_workers=None, what=""):
     out, lse = d.run(num_workers)
     ro, rl = _oracle_all(w)
     return compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, _tol(w), what or w.name)
-
-
-def _check_sampled(w, seqs, num_workers=None):
-    d = Dev(w)
-    out, lse = d.run(num_workers)
-    out = out.cpu().numpy()
-    lse = lse.cpu().numpy()
-    ro, rl = _oracle_all(w, seqs)
-    seqs = list(seqs)
-    return compare(out[seqs], lse[seqs], ro[seqs], rl[seqs], _tol(w), f"{w.name} seqs {seqs}")
 
 
 # ----------------------------------------------------------------------------- plan
@@ -246,14 +236,15 @@ def test_poison_does_not_propagate():
     assert torch.equal(op_, oc) and torch.equal(lp, lc)
 
 
-def test_page_ids_out_of_range_read_as_zeros():
-    """A block-table entry outside [0, num_pages) must not fault; those rows read as zeros."""
+def test_page_ids_out_of_range_read_as_zeros_and_are_reported():
+    """A block-table entry outside [0, num_pages) must not fault: those rows read as zeros, and
+    the call sets MLA_DEVICE_PAGE_OUT_OF_RANGE in its status word."""
     w = wl.make_workload("oob", batch=2, s_q=1, heads=128, seqlens=[192, 64], seed=27, poison=False)
     bad = w.block_table.copy()
     bad[0, 1] = w.num_pages + 1000
     w2 = wl.Workload(**{**w.__dict__, "block_table": bad})
     _say("oob page id")
-    out, lse = Dev(w2).run(4)
+    out, lse = Dev(w2).run(4, expect_status=2)
     kv0 = np.concatenate([w.kv, np.zeros((1,) + w.kv.shape[1:], dtype=w.kv.dtype)])
     bt0 = bad.copy()
     bt0[0, 1] = w.num_pages
@@ -264,14 +255,14 @@ def test_page_ids_out_of_range_read_as_zeros():
 @pytest.mark.parametrize("s_q,causal", [(1, False), (4, True)])
 def test_lengths_beyond_block_table_capacity(s_q, causal):
     """A length above max_pages * 64 reads as max_pages * 64 (the documented cap): same result
-    as the oracle run at the capped length."""
+    as the oracle run at the capped length, and MLA_DEVICE_LENGTH_OVER_CAPACITY is reported."""
     w = wl.make_workload("cap", batch=2, s_q=s_q, heads=32, seqlens=[150, 70], causal=causal, seed=28,
                          poison=False)
     cap = w.block_table.shape[1] * 64
     capped = wl.Workload(**{**w.__dict__, "seqlens": np.array([cap, 70], dtype=w.seqlens.dtype)})
     beyond = wl.Workload(**{**w.__dict__, "seqlens": np.array([cap + 40, 70], dtype=w.seqlens.dtype)})
     _say("lengths beyond capacity", s_q, causal)
-    out, lse = Dev(beyond).run(5)
+    out, lse = Dev(beyond).run(5, expect_status=4)
     ro, rl = _oracle_all(capped)
     compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, BF16_TOL, f"beyond capacity s_q={s_q}")
 
@@ -321,24 +312,159 @@ def test_graph_capture_replays_match_eager():
 
 # ----------------------------------------------------------------------------- full-size workloads
 
-def test_dsv3_full_size_sampled():
-    w = wl.make_config("dsv3")
-    _say("dsv3 full size")
-    _check_sampled(w, [0, 17, 63])
+def _check_all_sequences(w):
+    """Every output element of a full-size workload against the oracle (the oracle takes a few
+    seconds per workload on the host cores)."""
+    d = Dev(w)
+    out, lse = d.run()
+    ro, rl = _oracle_all(w)
+    return compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, _tol(w), f"{w.name} seed {w.seed} all sequences")
 
 
-def test_speculative_full_size_sampled():
-    w = wl.make_config("spec")
-    _say("spec full size")
-    _check_sampled(w, [0, 31])
+@pytest.mark.parametrize("seed", [None, 2001])
+def test_dsv3_full_size(seed):
+    w = wl.make_config("dsv3", seed=seed)
+    _say("dsv3 full size, seed", w.seed)
+    _check_all_sequences(w)
 
 
-def test_jagged_full_size_sampled():
-    w = wl.make_config("jagged")
-    lens = w.seqlens
-    pick = [int(np.argmax(lens)), int(np.argmin(lens)), int(np.argsort(lens)[len(lens) // 2])]
-    _say("jagged full size, seqs", pick, "lens", [int(lens[i]) for i in pick])
-    _check_sampled(w, pick)
+@pytest.mark.parametrize("seed", [None, 2003])
+def test_speculative_full_size(seed):
+    w = wl.make_config("spec", seed=seed)
+    _say("spec full size, seed", w.seed)
+    _check_all_sequences(w)
+
+
+@pytest.mark.parametrize("seed", [None, 2002])
+def test_jagged_full_size(seed):
+    w = wl.make_config("jagged", seed=seed)
+    _say("jagged full size, seed", w.seed, "total tokens", int(w.seqlens.sum()))
+    _check_all_sequences(w)
+
+
+@pytest.mark.parametrize("heads,s_q", [(128, 32), (128, 64), (16, 32), (16, 64)])
+def test_many_query_tokens_causal(heads, s_q):
+    """s_q up to the ABI's 64 under the causal reading: with h = 128 a sequence has s_q tiles
+    of one query token each, with h = 16 one tile holds 8 query tokens. Lengths below, at and
+    above s_q, several pages, and enough workers to split the long items."""
+    lens = [s_q - 5, s_q, s_q + 1, 300, 2100]
+    w = wl.make_workload("many-q", batch=5, s_q=s_q, heads=heads, seqlens=lens, causal=True, seed=40 + heads + s_q)
+    _say("many query tokens", heads, s_q)
+    _check_full(w, num_workers=64, what=f"h={heads} s={s_q} causal")
+
+
+# ----------------------------------------------------------------------------- split merge, plan reuse, device checks
+
+@pytest.mark.parametrize("W", [8, 24, 96, 256])
+def test_split_items_at_several_worker_counts(W):
+    """One batch with a long sequence split over many workers beside short ones split a few
+    ways or not at all, at worker counts that put the parts of an item on one XCD or on
+    several (blocks are dealt to the XCDs round-robin); every output against the oracle."""
+    w = wl.make_workload("splits", batch=6, s_q=1, heads=128, seqlens=[20000, 3000, 2500, 700, 64, 1], seed=41)
+    d = Dev(w)
+    ro, rl = _oracle_all(w)
+    plan = d.plan(W)
+    nsplits = plan.buffer.view(torch.int32).cpu().numpy()[16:16 + 8 * 6].reshape(6, 8)[:, 6]
+    assert (nsplits > 1).any(), nsplits
+    _say("split items, W", W, "parts", nsplits.tolist())
+    o, l = d.run(plan=plan)
+    compare(o.cpu().numpy(), l.cpu().numpy(), ro, rl, BF16_TOL, f"splits W={W}")
+
+
+def test_plan_reused_across_calls():
+    """One plan serves many calls (as one plan serves every layer of a decode step): five calls,
+    outputs NaN before each, all bitwise equal and matching the oracle."""
+    w = wl.make_workload("reuse", batch=8, s_q=1, heads=128, seqlens=[4096] * 6 + [900, 33], seed=42)
+    d = Dev(w)
+    plan = d.plan(256)
+    ro, rl = _oracle_all(w)
+    first = None
+    for r in range(5):
+        _say("plan reuse call", r)
+        o, l = d.run(plan=plan)
+        if first is None:
+            first = (o, l)
+            compare(o.cpu().numpy(), l.cpu().numpy(), ro, rl, BF16_TOL, "plan reuse")
+        else:
+            assert torch.equal(o, first[0]) and torch.equal(l, first[1]), f"call {r} differs"
+
+
+def test_mismatched_plan_is_reported_and_writes_nothing(monkeypatch):
+    """A plan built for 8 workers, in a buffer sized for 16, passed with num_workers = 16 (the
+    binding checks the buffer size only): the decode and combine kernels check the plan header,
+    write nothing (out and
+    lse, carved from a guarded buffer, keep their NaN; the guard bytes around them keep their
+    values), and set MLA_DEVICE_PLAN_MISMATCH. With MLA_VALIDATE=1 the call returns
+    MLA_ERR_INVALID_ARG instead of MLA_OK."""
+    w = wl.make_workload("mismatch", batch=3, s_q=1, heads=128, seqlens=[700, 64, 3000], seed=43)
+    d = Dev(w)
+    big = torch.zeros(mla.plan_bytes(w.batch, 1, 128, 16), dtype=torch.uint8, device="cuda")
+    built = mla.get_split_plan(d.sl, 1, 128, False, 8, out=big)
+    bad = mla.SplitPlan(built.buffer, built.batch, built.s_q, built.heads, built.causal, 16)
+    good = d.plan(8)
+    n_out, n_lse = w.batch * 128 * 512, w.batch * 128
+    guard = 4096
+    buf = torch.full((guard + n_out + guard + n_lse + guard,), 7.0, dtype=torch.float32, device="cuda")
+    out = buf[guard:guard + n_out].view(w.batch, 1, 128, 512)
+    lse = buf[2 * guard + n_out:2 * guard + n_out + n_lse].view(w.batch, 1, 128)
+    out.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _say("mismatched plan")
+    mla.decode_fwd(d.q, d.kv, d.bt, d.sl, w.scale, plan=bad, out=out, lse=lse, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1
+    assert torch.isnan(out).all() and torch.isnan(lse).all()
+    g = torch.cat([buf[:guard], buf[guard + n_out:2 * guard + n_out], buf[2 * guard + n_out + n_lse:]])
+    assert (g == 7.0).all()
+    monkeypatch.setenv("MLA_VALIDATE", "1")
+    with pytest.raises(mla.MlaError) as ei:
+        mla.decode_fwd(d.q, d.kv, d.bt, d.sl, w.scale, plan=bad, out=out, lse=lse)
+    assert ei.value.status == 1 and "plan" in str(ei.value)
+    # and a correct call passes validation
+    o, l = mla.decode_fwd(d.q, d.kv, d.bt, d.sl, w.scale, plan=good)
+    ro, rl = _oracle_all(w)
+    compare(o.cpu().numpy(), l.cpu().numpy(), ro, rl, BF16_TOL, "validated call")
+
+
+def test_validate_reports_out_of_range_pages(monkeypatch):
+    """MLA_VALIDATE=1 turns a block-table entry outside the cache into MLA_ERR_INVALID_ARG."""
+    w = wl.make_workload("oob-validate", batch=2, s_q=1, heads=32, seqlens=[192, 64], seed=44, poison=False)
+    bad = w.block_table.copy()
+    bad[1, 0] = -5
+    d = Dev(wl.Workload(**{**w.__dict__, "block_table": bad}))
+    monkeypatch.setenv("MLA_VALIDATE", "1")
+    _say("validate oob")
+    with pytest.raises(mla.MlaError) as ei:
+        mla.decode_fwd(d.q, d.kv, d.bt, d.sl, w.scale, plan=d.plan(4))
+    assert "outside [0, num_pages)" in str(ei.value)
+
+
+def test_binding_rejects_wrong_shapes():
+    """Every tensor of decode_fwd is checked before the C call (wrong shape, dtype or size ->
+    ValueError; nothing is launched)."""
+    w = wl.make_workload("shapes", batch=2, s_q=1, heads=16, seqlens=[100, 64], seed=45)
+    d = Dev(w)
+    plan = d.plan(4)
+    ok = dict(q=d.q, kv_cache=d.kv, block_table=d.bt, seqlens=d.sl, softmax_scale=w.scale, plan=plan)
+    cases = {
+        "q last dim": dict(q=d.q[..., :512].contiguous()),
+        "flattened cache": dict(kv_cache=d.kv.view(-1, 576)),
+        "cache row width": dict(kv_cache=d.kv.view(-1, 32, 1152)),
+        "bf16 with scales": dict(kv_scales=torch.ones(d.kv.shape[0], 64, 4, device="cuda")),
+        "table rows": dict(block_table=d.bt[:1].contiguous()),
+        "seqlens length": dict(seqlens=torch.cat([d.sl, d.sl])),
+        "out shape": dict(out=torch.empty(2, 1, 16, 128, device="cuda")),
+        "lse dtype": dict(lse=torch.empty(2, 1, 16, dtype=torch.float64, device="cuda")),
+        "workspace size": dict(workspace=torch.empty(16, dtype=torch.uint8, device="cuda")),
+        "status dtype": dict(status=torch.zeros(1, dtype=torch.int64, device="cuda")),
+    }
+    for name, kw in cases.items():
+        with pytest.raises(ValueError):
+            mla.decode_fwd(**{**ok, **kw})
+        assert name
+    mla.decode_fwd(**ok)
+    torch.cuda.synchronize()
 
 
 # ----------------------------------------------------------------------------- fp8 cache
@@ -375,8 +501,9 @@ def test_fp8_empty_and_bitwise_repeat():
     assert (o1[0] == 0).all()
 
 
-def test_fp8_full_size_sampled():
-    """64 sequences of 32,768 tokens, fp8 cache; every row of three sequences."""
-    w = wl.make_config("fp8")
-    _say("fp8 full size")
-    _check_sampled(w, [0, 29, 63])
+@pytest.mark.parametrize("seed", [None, 2004])
+def test_fp8_full_size(seed):
+    """64 sequences of 32,768 tokens, fp8 cache; every output element."""
+    w = wl.make_config("fp8", seed=seed)
+    _say("fp8 full size, seed", w.seed)
+    _check_all_sequences(w)

@@ -2,8 +2,9 @@
 Efficient Multi-head Latent Attention Kernels": sparse attention over selected tokens in
 decoding) against the fp64 oracle, through the C ABI: lists shorter and longer than a
 32-token step, random order, duplicates, padding entries, empty lists, query tokens of one
-sequence with different lists, several worker counts (split lists), a bitwise repeat, and
-sampled rows at the full V3.2-like size. Held to the fp8 bounds of the dense decode."""
+sequence with different lists, several worker counts (split lists), a bitwise repeat, every
+row at the full V3.2-like size, and a listed key whose page id is outside the cache (reported
+in the status word). Held to the fp8 bounds of the dense decode."""
 import numpy as np
 import pytest
 import torch
@@ -20,12 +21,18 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _run(w, idx, num_workers=None):
+def _run(w, idx, num_workers=None, expect_status=0):
+    """Row lists, plan and decode; out and lse start as NaN and the status word must read
+    expect_status afterwards."""
     d = Dev(w)
     ind = torch.from_numpy(idx).cuda()
-    plan = mla.get_sparse_plan(ind, d.bt, d.sl, int(w.kv.shape[0]), w.heads, num_workers)
-    out, lse = mla.sparse_decode_fwd(d.q, d.kv, d.scales, w.scale, plan)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plan = mla.get_sparse_plan(ind, d.bt, d.sl, int(w.kv.shape[0]), w.heads, num_workers, status=status)
+    out = torch.full((w.batch, w.s_q, w.heads, 512), float("nan"), device="cuda")
+    lse = torch.full((w.batch, w.s_q, w.heads), float("nan"), device="cuda")
+    mla.sparse_decode_fwd(d.q, d.kv, d.scales, w.scale, plan, out=out, lse=lse, status=status)
     torch.cuda.synchronize()
+    assert int(status.item()) == expect_status, int(status.item())
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
@@ -62,16 +69,34 @@ def test_sparse_empty_lists_and_bitwise_repeat():
     compare(o1, l1, ro, rl, FP8_TOL, "sparse empty")
 
 
-def test_sparse_full_size_sampled():
-    """64 sequences of 32,768 fp8 tokens, 2,048 selected tokens per query token; every row of
-    three sequences against the oracle."""
+def test_sparse_full_size():
+    """64 sequences of 32,768 fp8 tokens, 2,048 selected tokens per query token; every output
+    element against the oracle."""
     w = wl.make_config("fp8")
     idx = wl.make_sparse_indices(w.seqlens, w.s_q, 2048, seed=93)
     _say("sparse full size")
     out, lse = _run(w, idx)
-    seqs = [0, 31, 63]
-    ro, rl = om.decode_sparse(w.q, w.kv, w.kv_scales, "fp8", w.block_table, w.seqlens, idx, w.scale, seqs=seqs)
-    compare(out[seqs], lse[seqs], ro[seqs], rl[seqs], FP8_TOL, "sparse full size")
+    ro, rl = om.decode_sparse(w.q, w.kv, w.kv_scales, "fp8", w.block_table, w.seqlens, idx, w.scale)
+    compare(out, lse, ro, rl, FP8_TOL, "sparse full size")
+
+
+def test_sparse_page_out_of_range_reads_as_zeros_and_is_reported():
+    """A listed key on a page whose block-table entry is outside [0, num_pages): that key reads
+    as a zero row, and the row lists set MLA_DEVICE_PAGE_OUT_OF_RANGE."""
+    w = wl.make_workload("sparse-oob", batch=2, s_q=1, heads=128, seqlens=[200, 100], kv_dtype="fp8", seed=96,
+                         poison=False)
+    bad = w.block_table.copy()
+    bad[0, 1] = w.num_pages + 7
+    w2 = wl.Workload(**{**w.__dict__, "block_table": bad})
+    idx = wl.make_sparse_indices(w.seqlens, 1, 150, seed=97)
+    _say("sparse oob page")
+    out, lse = _run(w2, idx, 8, expect_status=2)
+    kv0 = np.concatenate([w.kv, np.zeros((1,) + w.kv.shape[1:], dtype=w.kv.dtype)])
+    sc0 = np.concatenate([w.kv_scales, np.zeros((1,) + w.kv_scales.shape[1:], dtype=w.kv_scales.dtype)])
+    bt0 = bad.copy()
+    bt0[0, 1] = w.num_pages
+    ro, rl = om.decode_sparse(w.q, kv0, sc0, "fp8", bt0, w.seqlens, idx, w.scale)
+    compare(out, lse, ro, rl, FP8_TOL, "sparse oob")
 
 
 @pytest.mark.parametrize("W", [1, 256])
