@@ -160,6 +160,25 @@ int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scal
                        void* workspace, size_t workspace_bytes, float* out, float* lse, int32_t* status,
                        void* stream);
 
+/* mla_decode_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation, kernels and
+ * arguments, with the split partials kept in a scratch array the library owns instead of a
+ * caller workspace. The array, MLA_NOALLOC_SCRATCH_BYTES bytes, is a static device array: each
+ * GPU the library runs on holds its own copy until the process ends, and its address is taken
+ * once per device at the first call on it. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine). Nothing in the scratch needs to start at zero: the decode
+ * kernel writes every partial before the combine kernel reads it.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (other
+ * streams, other threads) race. A shape whose workspace (mla_workspace_bytes) exceeds
+ * MLA_NOALLOC_SCRATCH_BYTES -- more than 286 workers -- returns MLA_ERR_WORKSPACE_TOO_SMALL
+ * before anything is enqueued. Arguments and errors otherwise as for mla_decode_fwd. */
+#define MLA_NOALLOC_SCRATCH_BYTES (72u << 20)
+int32_t mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const float* kv_scales, int32_t kv_dtype,
+                               int64_t num_pages, const int32_t* block_table, int32_t max_pages,
+                               const int32_t* seqlens, int32_t batch, int32_t s_q, int32_t heads,
+                               float softmax_scale, int32_t causal, const void* plan, int32_t num_workers,
+                               float* out, float* lse, int32_t* status, void* stream);
+
 /* Query absorption (page "Mla Analysis", section "Absorption Trick (FlashMLA)": scoring the
  * absorbed query against a latent row equals scoring the query against the decompressed
  * key). Per token t and head h:

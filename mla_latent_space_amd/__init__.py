@@ -19,11 +19,12 @@ import torch
 
 __all__ = ["MlaError", "SplitPlan", "lib", "abi_version", "default_num_workers", "plan_bytes", "workspace_bytes",
            "absorb_query", "decompress_output",
-           "get_split_plan", "decode_fwd", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3", "hybrid_merge", "SparsePlan", "get_sparse_plan", "sparse_decode_fwd"]
+           "get_split_plan", "decode_fwd", "decode_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3", "hybrid_merge", "SparsePlan", "get_sparse_plan", "sparse_decode_fwd"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
+NOALLOC_SCRATCH_BYTES = 72 << 20   # MLA_NOALLOC_SCRATCH_BYTES in include/libmla.h
 _STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_WORKSPACE_TOO_SMALL",
            4: "MLA_ERR_HIP", 5: "MLA_ERR_INTERNAL"}
 
@@ -62,6 +63,9 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_fwd.restype = c_i32
     L.mla_decode_fwd.argtypes = [c_p, c_p, c_p, c_i32, c_i64, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_f, c_i32,
                                  c_p, c_i32, c_p, c_sz, c_p, c_p, c_p, c_p]
+    L.mla_decode_fwd_noalloc.restype = c_i32
+    L.mla_decode_fwd_noalloc.argtypes = [c_p, c_p, c_p, c_i32, c_i64, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_f,
+                                         c_i32, c_p, c_i32, c_p, c_p, c_p, c_p]
     L.mla_absorb_query.restype = c_i32
     L.mla_absorb_query.argtypes = [c_p, c_p, c_p, c_i32, c_i32, c_p, c_p]
     L.mla_decompress_output.restype = c_i32
@@ -164,16 +168,8 @@ def _status_ptr(status: Optional[torch.Tensor], device):
     return status.data_ptr()
 
 
-def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor,
-               softmax_scale: float, kv_scales: Optional[torch.Tensor] = None, causal: bool = False,
-               plan: Optional[SplitPlan] = None, workspace: Optional[torch.Tensor] = None,
-               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-               status: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Latent-space MLA decode (see mla_decode_fwd). q: bf16 [b, s, h, 576]; kv_cache: bf16
-    [pages, 64, 576] or uint8 [pages, 64, 640] with kv_scales float32 [pages, 64, 4];
-    block_table int32 [b, max_pages]; seqlens int32 [b]. Returns out float32 [b, s, h, 512]
-    and lse float32 [b, s, h]. `status`, an int32 CUDA tensor, receives the device-side
-    MLA_DEVICE_* bits in its first element (OR-ed, never cleared)."""
+def _decode_args(q, kv_cache, block_table, seqlens, kv_scales, causal, plan, out, lse, status):
+    """Checks every tensor of a decode call; returns (kv_dtype, plan, out, lse, status pointer)."""
     if q.dim() != 4 or q.shape[-1] != 576:
         raise ValueError("q must be [batch, s_q, heads, 576]")
     batch, s_q, heads, _ = (int(x) for x in q.shape)
@@ -203,26 +199,60 @@ def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         plan = get_split_plan(seqlens, s_q, heads, causal)
     if (plan.batch, plan.s_q, plan.heads, plan.causal) != (batch, s_q, heads, bool(causal)):
         raise ValueError("plan was built for different arguments")
-    W = plan.num_workers
-    _need_bytes(plan.buffer, "plan buffer", plan_bytes(batch, s_q, heads, W), dev)
-    need = workspace_bytes(batch, s_q, heads, W)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    if workspace is not None:
-        _need_bytes(workspace, "workspace", need, dev)
+    _need_bytes(plan.buffer, "plan buffer", plan_bytes(batch, s_q, heads, plan.num_workers), dev)
     if out is None:
         out = torch.empty(batch, s_q, heads, 512, dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty(batch, s_q, heads, dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, (batch, s_q, heads, 512), dev)
     _need(lse, "lse", torch.float32, (batch, s_q, heads), dev)
-    status_ptr = _status_ptr(status, dev)
+    return kv_dtype, plan, out, lse, _status_ptr(status, dev)
+
+
+def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor,
+               softmax_scale: float, kv_scales: Optional[torch.Tensor] = None, causal: bool = False,
+               plan: Optional[SplitPlan] = None, workspace: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               status: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Latent-space MLA decode (see mla_decode_fwd). q: bf16 [b, s, h, 576]; kv_cache: bf16
+    [pages, 64, 576] or uint8 [pages, 64, 640] with kv_scales float32 [pages, 64, 4];
+    block_table int32 [b, max_pages]; seqlens int32 [b]. Returns out float32 [b, s, h, 512]
+    and lse float32 [b, s, h]. `status`, an int32 CUDA tensor, receives the device-side
+    MLA_DEVICE_* bits in its first element (OR-ed, never cleared)."""
+    kv_dtype, plan, out, lse, status_ptr = _decode_args(q, kv_cache, block_table, seqlens, kv_scales, causal, plan,
+                                                        out, lse, status)
+    batch, s_q, heads = plan.batch, plan.s_q, plan.heads
+    W = plan.num_workers
+    need = workspace_bytes(batch, s_q, heads, W)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need_bytes(workspace, "workspace", need, q.device)
     rc = lib().mla_decode_fwd(
         q.data_ptr(), kv_cache.data_ptr(), None if kv_scales is None else kv_scales.data_ptr(), kv_dtype,
-        pages, block_table.data_ptr(), int(block_table.shape[1]), seqlens.data_ptr(), batch, s_q, heads,
-        float(softmax_scale), int(causal), plan.buffer.data_ptr(), W,
+        int(kv_cache.shape[0]), block_table.data_ptr(), int(block_table.shape[1]), seqlens.data_ptr(), batch, s_q,
+        heads, float(softmax_scale), int(causal), plan.buffer.data_ptr(), W,
         None if workspace is None else workspace.data_ptr(),
         0 if workspace is None else workspace.numel() * workspace.element_size(),
+        out.data_ptr(), lse.data_ptr(), status_ptr, _stream(q))
+    _check(int(rc))
+    return out, lse
+
+
+def decode_fwd_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor,
+                       softmax_scale: float, kv_scales: Optional[torch.Tensor] = None, causal: bool = False,
+                       plan: Optional[SplitPlan] = None, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None,
+                       status: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """decode_fwd with the split partials in the library's own scratch (see
+    mla_decode_fwd_noalloc): no workspace argument, nothing allocated by the library. Pass
+    `plan`, `out` and `lse` to allocate nothing here either."""
+    kv_dtype, plan, out, lse, status_ptr = _decode_args(q, kv_cache, block_table, seqlens, kv_scales, causal, plan,
+                                                        out, lse, status)
+    rc = lib().mla_decode_fwd_noalloc(
+        q.data_ptr(), kv_cache.data_ptr(), None if kv_scales is None else kv_scales.data_ptr(), kv_dtype,
+        int(kv_cache.shape[0]), block_table.data_ptr(), int(block_table.shape[1]), seqlens.data_ptr(), plan.batch,
+        plan.s_q, plan.heads, float(softmax_scale), int(causal), plan.buffer.data_ptr(), plan.num_workers,
         out.data_ptr(), lse.data_ptr(), status_ptr, _stream(q))
     _check(int(rc))
     return out, lse

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "libmla.h"
@@ -14,6 +15,11 @@
 // Library-owned device word (one copy per GPU, alive until the process ends): the status word
 // of calls validated without a caller status word.
 static __device__ int32_t g_validate_status;
+
+// Split-partial scratch of mla_decode_fwd_noalloc: one copy per GPU, held until the process
+// ends. Its device address is taken once per device (hipGetSymbolAddress, with that device
+// current) and that address, never the symbol, is what host code passes to the kernels.
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -35,6 +41,28 @@ int32_t ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Device address of `scratch` per device, taken at the first mla_decode_fwd_noalloc call on
+// that device.
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_ptr(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 bool env_flag(const char* name) {
   const char* e = std::getenv(name);
@@ -116,6 +144,72 @@ size_t workspace_bytes_of(int32_t batch, int32_t s_q, int32_t heads, int32_t wor
   return (size_t)slots * (size_t)mla::kSlotBytes;
 }
 
+// Host checks of a decode call beyond its shape; `need` is the workspace the shape requires.
+int32_t check_decode_args(const void* q, const void* kv_cache, const float* kv_scales, int32_t kv_dtype,
+                          int64_t num_pages, const int32_t* block_table, int32_t max_pages, const int32_t* seqlens,
+                          float softmax_scale, const void* plan, const void* workspace, size_t workspace_bytes,
+                          const float* out, const float* lse, const int32_t* status, size_t need) {
+  if (!q || !kv_cache || !block_table || !seqlens || !plan || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL (q, kv_cache, block_table, seqlens, plan, out, lse)");
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_INVALID_ARG, "kv_dtype must be MLA_KV_BF16 or MLA_KV_FP8_E4M3 (got %d)", kv_dtype);
+  if (kv_dtype == MLA_KV_FP8_E4M3 && !kv_scales)
+    return fail(MLA_ERR_INVALID_ARG, "kv_scales is required for an fp8 cache");
+  if (kv_dtype == MLA_KV_BF16 && kv_scales)
+    return fail(MLA_ERR_INVALID_ARG, "kv_scales must be NULL for a bf16 cache");
+  if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1 (got %lld)", (long long)num_pages);
+  if (max_pages < 1 || max_pages > mla::kMaxPagesPerSeq)
+    return fail(max_pages < 1 ? MLA_ERR_INVALID_ARG : MLA_ERR_UNSUPPORTED, "max_pages must be in 1..%d (got %d)",
+                mla::kMaxPagesPerSeq, max_pages);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) || !aligned16(plan) ||
+      (kv_scales && !aligned16(kv_scales)) || (workspace && !aligned16(workspace)))
+    return fail(MLA_ERR_INVALID_ARG, "q, kv_cache, kv_scales, out, plan and workspace must be 16-byte aligned");
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace ? workspace_bytes : 0,
+                need);
+  if (status && (reinterpret_cast<uintptr_t>(status) & 3u))
+    return fail(MLA_ERR_INVALID_ARG, "status must be 4-byte aligned");
+  return MLA_OK;
+}
+
+// Enqueue the decode kernel and the split combine of a checked call (workspace: the split
+// partials' device memory, caller-owned or the library's scratch).
+int32_t decode_launch(const void* q, const void* kv_cache, const float* kv_scales, int32_t kv_dtype, int64_t num_pages,
+                      const int32_t* block_table, int32_t max_pages, const int32_t* seqlens, int32_t batch,
+                      int32_t s_q, int32_t heads, float softmax_scale, int32_t causal, const void* plan,
+                      int32_t num_workers, void* workspace, float* out, float* lse, int32_t* status, void* stream,
+                      const char* call) {
+  mla::DecodeArgs a;
+  a.q = q;
+  a.kv = kv_cache;
+  a.kv_scales = kv_scales;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.seqlens = seqlens;
+  a.batch = batch;
+  a.s_q = s_q;
+  a.heads = heads;
+  a.causal = causal;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.plan = static_cast<const int32_t*>(plan);
+  a.workers = num_workers;
+  a.ws = static_cast<float*>(workspace);
+  a.out = out;
+  a.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool validating = false;
+  a.status = validate_begin(status, s, &validating);
+  hipError_t e = mla::launch_decode_rows32(a, kv_dtype == MLA_KV_FP8_E4M3, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
+  e = mla::launch_combine_rows32(a, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+  if (validating) return validate_end(a.status, s, call);
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,56 +274,41 @@ int32_t mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scal
                        float* lse, int32_t* status, void* stream) {
   int32_t st = check_shape(batch, s_q, heads, causal, num_workers);
   if (st != MLA_OK) return st;
-  if (!q || !kv_cache || !block_table || !seqlens || !plan || !out || !lse)
-    return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL (q, kv_cache, block_table, seqlens, plan, out, lse)");
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
-    return fail(MLA_ERR_INVALID_ARG, "kv_dtype must be MLA_KV_BF16 or MLA_KV_FP8_E4M3 (got %d)", kv_dtype);
-  if (kv_dtype == MLA_KV_FP8_E4M3 && !kv_scales)
-    return fail(MLA_ERR_INVALID_ARG, "kv_scales is required for an fp8 cache");
-  if (kv_dtype == MLA_KV_BF16 && kv_scales)
-    return fail(MLA_ERR_INVALID_ARG, "kv_scales must be NULL for a bf16 cache");
-  if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1 (got %lld)", (long long)num_pages);
-  if (max_pages < 1 || max_pages > mla::kMaxPagesPerSeq)
-    return fail(max_pages < 1 ? MLA_ERR_INVALID_ARG : MLA_ERR_UNSUPPORTED, "max_pages must be in 1..%d (got %d)",
-                mla::kMaxPagesPerSeq, max_pages);
-  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
-    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
-  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) || !aligned16(plan) ||
-      (kv_scales && !aligned16(kv_scales)) || (workspace && !aligned16(workspace)))
-    return fail(MLA_ERR_INVALID_ARG, "q, kv_cache, kv_scales, out, plan and workspace must be 16-byte aligned");
+  st = check_decode_args(q, kv_cache, kv_scales, kv_dtype, num_pages, block_table, max_pages, seqlens, softmax_scale,
+                         plan, workspace, workspace_bytes, out, lse, status,
+                         workspace_bytes_of(batch, s_q, heads, num_workers));
+  if (st != MLA_OK) return st;
+  return decode_launch(q, kv_cache, kv_scales, kv_dtype, num_pages, block_table, max_pages, seqlens, batch, s_q,
+                       heads, softmax_scale, causal, plan, num_workers, workspace, out, lse, status, stream,
+                       "mla_decode_fwd");
+}
+
+int32_t mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const float* kv_scales, int32_t kv_dtype,
+                               int64_t num_pages, const int32_t* block_table, int32_t max_pages,
+                               const int32_t* seqlens, int32_t batch, int32_t s_q, int32_t heads,
+                               float softmax_scale, int32_t causal, const void* plan, int32_t num_workers,
+                               float* out, float* lse, int32_t* status, void* stream) {
+  int32_t st = check_shape(batch, s_q, heads, causal, num_workers);
+  if (st != MLA_OK) return st;
   const size_t need = workspace_bytes_of(batch, s_q, heads, num_workers);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes %zu < required %zu", workspace ? workspace_bytes : 0,
-                need);
-  mla::DecodeArgs a;
-  a.q = q;
-  a.kv = kv_cache;
-  a.kv_scales = kv_scales;
-  a.num_pages = num_pages;
-  a.block_table = block_table;
-  a.max_pages = max_pages;
-  a.seqlens = seqlens;
-  a.batch = batch;
-  a.s_q = s_q;
-  a.heads = heads;
-  a.causal = causal;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.plan = static_cast<const int32_t*>(plan);
-  a.workers = num_workers;
-  a.ws = static_cast<float*>(workspace);
-  a.out = out;
-  a.lse = lse;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (status && (reinterpret_cast<uintptr_t>(status) & 3u))
-    return fail(MLA_ERR_INVALID_ARG, "status must be 4-byte aligned");
-  bool validating = false;
-  a.status = validate_begin(status, s, &validating);
-  hipError_t e = mla::launch_decode_rows32(a, kv_dtype == MLA_KV_FP8_E4M3, s);
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
-  e = mla::launch_combine_rows32(a, s);
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
-  if (validating) return validate_end(a.status, s, "mla_decode_fwd");
-  return ok();
+  if (need > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "mla_decode_fwd_noalloc: this shape needs %zu bytes of split scratch, more than the library's "
+                "%zu (use fewer workers, or mla_decode_fwd with a workspace)",
+                need, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  // every argument check of mla_decode_fwd before the scratch address is taken (a stand-in
+  // workspace pointer; nothing is launched when a check fails)
+  void* ws = need > 0 ? reinterpret_cast<void*>(static_cast<uintptr_t>(256)) : nullptr;
+  st = check_decode_args(q, kv_cache, kv_scales, kv_dtype, num_pages, block_table, max_pages, seqlens, softmax_scale,
+                         plan, ws, need, out, lse, status, need);
+  if (st != MLA_OK) return st;
+  if (need > 0) {
+    hipError_t e = scratch_ptr(&ws);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
+  }
+  return decode_launch(q, kv_cache, kv_scales, kv_dtype, num_pages, block_table, max_pages, seqlens, batch, s_q,
+                       heads, softmax_scale, causal, plan, num_workers, ws, out, lse, status, stream,
+                       "mla_decode_fwd_noalloc");
 }
 
 int32_t mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int32_t tokens, int32_t heads,
