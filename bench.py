@@ -453,20 +453,22 @@ def main():
     # stream around K back-to-back calls (the plan once per decode step, the decode once per
     # layer of that step, so the decode calls reuse one plan)
     stream = torch.cuda.current_stream()
+    # (at least 200 calls each, so that a short run still averages over a steady state)
     plan = mla.get_split_plan(sl, w.s_q, w.heads, w.causal, W, out=plan_buf)
+    n_calls = max(args.steps, 200)
     e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     torch.cuda.synchronize()
     e0.record(stream)
-    for i in range(args.steps):
+    for i in range(n_calls):
         mla.decode_fwd(q, kvs[i % rot], bt, sl, w.scale, kv_scales=scs[i % rot], causal=w.causal, plan=plan,
                        workspace=ws, out=out, lse=lse)
     e1.record(stream)
-    for i in range(args.steps):
+    for i in range(n_calls):
         mla.get_split_plan(sl, w.s_q, w.heads, w.causal, W, out=plan_buf)
     e2.record(stream)
     torch.cuda.synchronize()
-    dec_mean = e0.elapsed_time(e1) * 1e3 / args.steps
-    plan_mean = e1.elapsed_time(e2) * 1e3 / args.steps
+    dec_mean = e0.elapsed_time(e1) * 1e3 / n_calls
+    plan_mean = e1.elapsed_time(e2) * 1e3 / n_calls
 
     flops = workload_flops(w)
     byts = workload_bytes(w)
