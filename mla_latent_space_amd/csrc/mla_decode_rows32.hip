@@ -514,41 +514,57 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
 #pragma unroll 1
     for (int r = 0; r < 4; ++r) dma_rows(r);
   }
-  // Start-up: the first item's 128 query rows (147 KB, contiguous in q) are staged through
-  // the four ring slots by LDS-DMA, 32 rows per slot in the cache-step layout, and each wave
-  // reads its 32 rows back with the score-operand read pattern. (Loaded straight into
-  // registers, each load instruction would touch 32 rows; with every worker starting at
-  // once, that burst is bound by the number of cache lines.) Rows past the last query row
-  // read as zeros. Then the first ring steps.
+  int comp_slot = 0;   // ring slot of the segment's current step
+  // Start-up, for the first item. Its query rows are staged through LDS by LDS-DMA, 32 rows
+  // per ring slot in the cache-step layout, and each wave reads its 32 rows back with the
+  // score-operand read pattern; rows past the last query row read as zeros. (Loaded straight
+  // into registers, each load instruction touches 32 rows; with every worker starting at
+  // once, that burst is bound by the number of cache lines.)
+  //  * bf16 cache: the rows of waves 0..2 go through slots 0..2 while the first ring step is
+  //    already loading into slot 3 (the ring starts there), and wave 3 loads its 32 rows into
+  //    registers; then the next two ring steps go into slots 0 and 1.
+  //  * fp8 cache: all four waves' rows through the four slots, then the fp8 pipeline fill.
   auto start_up = [&]() {
     const int32_t* it = plan + plan_items_off() + kItemWords * kb;
     const int tile0 = kRowsPerTile * it[kITile];
     const int valid_rows = rows_total - tile0 < kRowsPerTile ? rows_total - tile0 : kRowsPerTile;
     const uint64_t qbase = reinterpret_cast<uint64_t>(q_ptr) +
                            ((uint64_t)it[kISeq] * (uint64_t)rows_total + (uint64_t)tile0) * kRowBytes;
+    constexpr int kStaged = kFp8 ? kR32Slots : kR32Slots - 1;   // slots (waves) staged by DMA
 #pragma unroll 1
-    for (int sl = 0; sl < kR32Slots; ++sl) {
+    for (int sl = 0; sl < kStaged; ++sl) {
       int bytes = valid_rows * kRowBytes - sl * kBufBytes;
       bytes = bytes < 0 ? 0 : (bytes > kBufBytes ? kBufBytes : bytes);
       const i32x4 rs = make_rsrc(qbase + (uint64_t)sl * kBufBytes, bytes);
 #pragma unroll
       for (int n = 0; n < kR32Dma; ++n) issue32(rs, lds_u32 + sl * kBufBytes, n, dma_voff(dmo, n), wave);
     }
-    wait_vmcnt<0>();
+    if constexpr (!kFp8) {
+      load_slot = kR32Slots - 1;   // the first ring step into the free slot
+      comp_slot = kR32Slots - 1;
+      issue_step();
+      wait_vmcnt<kR32Dma>();       // this wave's staging DMA done (the ring step may stay in flight)
+    } else {
+      wait_vmcnt<0>();
+    }
     barrier_lds();
-    const QkAddr qa = qk_at(qk0, (uint32_t)wave * kBufBytes);
+    if (kFp8 || wave < kStaged) {
+      const QkAddr qa = qk_at(qk0, (uint32_t)wave * kBufBytes);
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) qreg[ks] = lds_b128(lds + (qa.b[ks & 3] + 128 * (ks >> 2)));
+      for (int ks = 0; ks < 36; ++ks) qreg[ks] = lds_b128(lds + (qa.b[ks & 3] + 128 * (ks >> 2)));
+    } else {
+      // (bf16) the last wave's rows straight into registers: the compiler waits for these
+      // loads at their first use
+      load_q(kb);
+    }
     barrier_lds();   // every wave holds its rows before the ring is refilled
     if constexpr (kFp8) {
       f8_fill(true);
     } else {
 #pragma unroll 1
-      for (int i = 0; i < kR32Slots - 1; ++i) issue_step();
+      for (int i = 0; i < kR32Slots - 2; ++i) issue_step();
     }
   };
-
-  int comp_slot = 0;   // ring slot of the segment's current step
 
 #pragma unroll 1
   for (int k = kb; k <= k_last; ++k) {
