@@ -13,13 +13,14 @@ no code with it: it imports nothing from ``mla_latent_space_amd``. Inputs reach 
 as plain arrays produced by the seeded generator module.
 
 Modules:
-  mla   -- latent-form decode, explicit (decompressed) form, e4m3fn decoder,
-           split combine, cost models.
+  mla   -- latent-form decode, explicit (decompressed) form, e4m3fn decoder and
+           the FP8-to-BF16 scaling, split combine, cost models.
   plan  -- the split-plan definition (sort by length, equal-cost contiguous
            chunks), used to check the device planner bit for bit.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
-(library cross-checks, closed forms, brute force, invariants, printed values, and
-for the cost models an independent tensor inventory), and each pin group has a
-planted-mistake test that must fail it. No function is "parity unpinned".
+(library cross-checks -- torch's float8 and bfloat16 casts for the number formats --,
+closed forms, brute force, invariants, printed values, and for the cost models an
+independent tensor inventory), and each pin group has a planted-mistake test that
+must fail it. No function is "parity unpinned".
 """

@@ -20,8 +20,9 @@ description and use cases: token-level sparse attention for decoding, with an FP
 (decode_sparse).
 
 FlashMLA-2 newsletter page, section "Architectural Analysis": the latent cache may be
-stored in FP8 and scaled up before the matrix products; OCP e4m3fn is the format read
-here, one float32 scale per token per 128-channel tile.
+stored in FP8 and is scaled from FP8 to BF16 in registers before the matrix products; OCP
+e4m3fn is the format read here, one float32 scale per token per 128-channel tile, and the
+value the products read is that BF16 number (fp8_dequant).
 
 Readings where the pages are silent (each listed in the design notes):
 * the log-sum-exp is the natural log of the sum of exp(scaled logits);
@@ -29,7 +30,9 @@ Readings where the pages are silent (each listed in the design notes):
 * with s > 1 query tokens and ``causal``, query j of a sequence with t cached
   tokens (which include the s new ones) sees keys 0 .. t - s + j;
 * an empty visible set gives out = 0 and lse = -inf;
-* the value is Z[:, :512] (rope excluded).
+* the value is Z[:, :512] (rope excluded);
+* the FP8-to-BF16 scaling forms code * scale in float32 (the scale's precision) and rounds
+  that product to the nearest BF16, ties to even.
 
 Everything is float64; no blocking, fusion or reordering beyond the definition.
 """
@@ -78,13 +81,34 @@ def e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
 _E4M3FN_VALUES = e4m3fn_to_f64(np.arange(256, dtype=np.uint8))
 
 
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> the nearest bf16 (ties to even), returned as float64. bf16 keeps the top 16
+    bits of a float32, so rounding adds half of the dropped range (0x7FFF, plus one when the
+    kept part is odd) to the bit pattern and truncates; the carry runs into the exponent, which
+    is the correct rounding at a binade edge. (Finite inputs; NaN is kept as NaN.)"""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(x), np.nan, out)
+
+
+def fp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The FP8-to-BF16 scaling of the FlashMLA-2 page ("Architectural Analysis"): each e4m3fn
+    code's value times its float32 scale, the product formed in float32 and rounded to bf16.
+    codes uint8 [..., n], scales float32 broadcastable to it; returns float64."""
+    v = _E4M3FN_VALUES[np.asarray(codes, dtype=np.uint8)].astype(np.float32)   # exact in float32
+    prod = v * np.asarray(scales, dtype=np.float32)                            # one float32 rounding
+    return f32_to_bf16(prod)
+
+
 # ----------------------------------------------------------------------------- cache gather
 
 def latent_rows(kv: np.ndarray, kv_scales: Optional[np.ndarray], kv_dtype: str,
                 block_table_row: np.ndarray, t: int) -> np.ndarray:
     """The first ``t`` cached rows of one sequence, gathered through its block table, as
-    float64 [t, 576]. fp8: row[c] = e4m3fn(code[c]) * scale[token, c // 128] for c < 512,
-    rope channels are bf16."""
+    float64 [t, 576]. fp8: row[c] = bf16(e4m3fn(code[c]) * scale[token, c // 128]) for
+    c < 512 (fp8_dequant), rope channels are bf16."""
     if t == 0:
         return np.zeros((0, D_QK))
     npages = (t + PAGE - 1) // PAGE
@@ -94,10 +118,10 @@ def latent_rows(kv: np.ndarray, kv_scales: Optional[np.ndarray], kv_dtype: str,
         return bf16_bits_to_f64(rows)
     if kv_dtype == "fp8":
         raw = kv[ids].reshape(npages * PAGE, -1)[:t]
-        sc = kv_scales[ids].reshape(npages * PAGE, K_LAT // FP8_TILE)[:t].astype(np.float64)
+        sc = kv_scales[ids].reshape(npages * PAGE, K_LAT // FP8_TILE)[:t]
         # channel c of a token times its tile's scale, tile = c // 128
-        lat = (_E4M3FN_VALUES[raw[:, :K_LAT]].reshape(t, K_LAT // FP8_TILE, FP8_TILE)
-               * sc[:, :, None]).reshape(t, K_LAT)
+        lat = fp8_dequant(raw[:, :K_LAT].reshape(t, K_LAT // FP8_TILE, FP8_TILE),
+                          sc[:, :, None]).reshape(t, K_LAT)
         rope = bf16_bits_to_f64(np.ascontiguousarray(raw[:, K_LAT:]).view(np.uint16))
         return np.concatenate([lat, rope], axis=1)
     raise ValueError(kv_dtype)

@@ -6,20 +6,18 @@ import torch
 
 import mla_latent_space_amd as mla
 
-# Tolerances on out (float32 [b, s, h, 512]) and lse. bf16 cache: rel L2 <= 5e-3, max abs
-# <= 2e-2, |d lse| <= 1e-3. fp8 cache: compared with the oracle on the same dequantised
-# values, rel L2 <= 3e-2 (the stated fp8 bound). Its max abs and lse bounds follow from
-# the arithmetic: the kernel dequantises each value once into bf16 (relative error
-# <= 2^-8, the unit roundoff of an 8-bit significand), which moves a score by at most
-# softmax_scale * 2^-8 * sum_c |q_c z_c| (about 1e-1 in the worst case and 6e-3 typical for
-# these N(0,1) draws, whose per-value errors have random signs); lse moves by no more than
-# the largest score error, so fp8 lse is held to 2e-2, about three times the typical
-# perturbation. out = sum_u p_u z_u with sum_u p_u = 1, and both z_u (the dequantised value)
-# and p_u are rounded once to bf16, so |d out_c| <= 2 * 2^-8 * max_u |z_uc| besides the
-# score term; the latent values of these workloads stay below 5 in magnitude, which gives
-# max abs <= 4e-2 (reached only by rows with a handful of visible keys).
+# Tolerances on out (float32 [b, s, h, 512]) and lse, one set for both cache types: the oracle
+# reads the operand values the kernel's matrix products read (bf16 queries; bf16 cache rows, or
+# fp8 rows after the FP8-to-BF16 scaling), so what differs is the kernel's own rounding: the
+# probabilities rounded to bf16 for the value product and the bf16 partial rows of split items
+# (each at most half a bf16 ulp, 2^-9 relative), and fp32 sums in another order. An output
+# element is a convex combination of latent values, so each rounding moves it by at most
+# 2^-9 * max |z|; with the latent values of these workloads below about 5 the two give
+# max abs <= 2e-2, reached only by rows with a few dominant keys (elsewhere the errors have
+# random signs and average out: rel L2 <= 5e-3). lse sees only the fp32 score sums and the
+# normaliser: |d lse| <= 1e-3.
 BF16_TOL = dict(rel_l2=5e-3, max_abs=2e-2, lse=1e-3)
-FP8_TOL = dict(rel_l2=3e-2, max_abs=4e-2, lse=2e-2)
+FP8_TOL = BF16_TOL
 
 
 class Dev:

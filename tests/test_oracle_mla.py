@@ -68,6 +68,49 @@ def test_e4m3_textbook_values():
     assert v[3] == 1.0 and v[4] == -1.0 and v[5] == 0.0 and v[6] == 0.0
 
 
+def _torch_bf16(x_f32):
+    return torch.from_numpy(np.ascontiguousarray(x_f32, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_f32_to_bf16_matches_torch_rounding():
+    """Round to nearest, ties to even, against torch's float32 -> bfloat16 cast: random bit
+    patterns of every magnitude, exact ties with an even and an odd kept part, values that
+    round up across a binade edge or overflow to infinity, subnormals and zeros."""
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 0x7F800000, 200000, dtype=np.int64).astype(np.uint32)
+    bits[::2] |= np.uint32(0x80000000)
+    ties = (rng.integers(0, 0x7F80, 2000, dtype=np.int64).astype(np.uint32) << 16) | np.uint32(0x8000)
+    edges = np.array([0x3F7FFFFF, 0x3F7F8000, 0x3F7F7FFF, 0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0x00000001,
+                      0x00008000, 0x00018000, 0x007FFFFF, 0x00000000, 0x80000000, 0xBF808000, 0xBF818000],
+                     dtype=np.uint32)
+    x = np.concatenate([bits, ties, edges]).view(np.float32)
+    mine, ref = om.f32_to_bf16(x), _torch_bf16(x)
+    assert np.array_equal(mine, ref)
+    assert om.f32_to_bf16(np.array([0x3F808000], dtype=np.uint32).view(np.float32))[0] == 1.0   # tie, even kept part
+    assert om.f32_to_bf16(np.array([0x3F818000], dtype=np.uint32).view(np.float32))[0] == 1.0 + 2 ** -6   # tie, odd
+    assert om.f32_to_bf16(np.array([0x7F7FFFFF], dtype=np.uint32).view(np.float32))[0] == np.inf
+
+
+def test_fp8_dequant_definition():
+    """bf16(fl32(e4m3fn(code) * scale)): equal to torch's float32 product cast to bf16 for all
+    256 codes at many scales; exact when the scale is a power of two; within one bf16 rounding
+    (2^-8 relative) of the exact product otherwise."""
+    rng = np.random.default_rng(8)
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]
+    scales = np.concatenate([rng.uniform(1e-4, 1.0, 200), rng.uniform(1.0, 50.0, 56)]).astype(np.float32)
+    got = om.fp8_dequant(codes[None, :], scales[:, None])
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32)
+    ref = (vals[None, :] * torch.from_numpy(scales)[:, None]).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, ref)
+    exact = om.e4m3fn_to_f64(codes)[None, :] * scales.astype(np.float64)[:, None]
+    assert np.all(np.abs(got - exact) <= 2.0 ** -8 * np.abs(exact) * (1 + 2.0 ** -20))
+    assert (got != exact).mean() > 0.5          # the rounding is real at these scales
+    p2 = np.array([2.0 ** -9, 2.0 ** -3, 1.0, 8.0], dtype=np.float32)
+    assert np.array_equal(om.fp8_dequant(codes[None, :], p2[:, None]),
+                          om.e4m3fn_to_f64(codes)[None, :] * p2.astype(np.float64)[:, None])
+
+
 def test_bf16_decode_matches_torch():
     rng = np.random.default_rng(1)
     bits = rng.integers(0, 0x7F80, 10000).astype(np.uint16)
@@ -226,9 +269,10 @@ def test_fp8_rows_match_torch_dequant():
         z = om.latent_rows(w.kv, w.kv_scales, "fp8", w.block_table[i], t)
         ids = w.block_table[i, :(t + 63) // 64]
         raw = torch.from_numpy(w.kv[ids].reshape(-1, 640)[:t].copy())
-        lat = raw[:, :512].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
-        sc = torch.from_numpy(w.kv_scales[ids].reshape(-1, 4)[:t].copy()).to(torch.float64)
-        lat = (lat.reshape(t, 4, 128) * sc[:, :, None]).reshape(t, 512)
+        # the FP8-to-BF16 scaling: float32 product, rounded to bf16
+        lat = raw[:, :512].contiguous().view(torch.float8_e4m3fn).to(torch.float32)
+        sc = torch.from_numpy(w.kv_scales[ids].reshape(-1, 4)[:t].copy())
+        lat = (lat.reshape(t, 4, 128) * sc[:, :, None]).reshape(t, 512).to(torch.bfloat16).to(torch.float64)
         rope = raw[:, 512:].contiguous().view(torch.bfloat16).to(torch.float64)
         ref = torch.cat([lat, rope], dim=1).numpy()
         assert np.array_equal(z, ref)
@@ -236,7 +280,8 @@ def test_fp8_rows_match_torch_dequant():
 
 def test_fp8_encoding_error_bound():
     """The generator's e4m3 encoding has relative step 2^-3 at most (3 mantissa bits), so each
-    dequantised value is within half an ulp: |x - x_hat| <= 2^-4 |x| for normals."""
+    decoded value is within half an ulp: |x - x_hat| <= 2^-4 |x| for normals; the bf16 rounding
+    of the scaled value adds at most 2^-8 of its magnitude."""
     w = _small(kv="fp8", seed=13, lens=(64,), b=1)
     z = om.latent_rows(w.kv, w.kv_scales, "fp8", w.block_table[0], 64)
     # regenerate the fp32 draws of the pool in the same order to compare
@@ -246,6 +291,7 @@ def test_fp8_encoding_error_bound():
     page0 = x[:64, :512]
     sc = w.kv_scales[w.block_table[0, 0]].astype(np.float64)
     tol = np.maximum(np.abs(page0) * 2.0 ** -4, np.repeat(sc, 128, axis=1) * 2.0 ** -10)
+    tol = tol + 2.0 ** -8 * (np.abs(page0) + tol)
     assert np.all(np.abs(z[:, :512] - page0) <= tol)
 
 
@@ -364,6 +410,29 @@ def _sdpa_pin_fails(w):
     except AssertionError:
         return True
     return False
+
+
+def test_pins_catch_truncating_bf16_rounding(monkeypatch):
+    """A planted mistake in the bf16 rounding (truncation instead of nearest-even) fails the
+    torch rounding pin and the dequant pin."""
+    def truncating(x):
+        x = np.asarray(x, dtype=np.float32)
+        return ((x.view(np.uint32) >> 16) << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    _mutant(monkeypatch, "f32_to_bf16", truncating)
+    with pytest.raises(AssertionError):
+        test_f32_to_bf16_matches_torch_rounding()
+    with pytest.raises(AssertionError):
+        test_fp8_dequant_definition()
+
+
+def test_pins_catch_unrounded_dequant(monkeypatch):
+    """A planted mistake that skips the bf16 rounding of the scaled value (the exact product)
+    fails the dequant pin and the cache-gather pin."""
+    _mutant(monkeypatch, "f32_to_bf16", lambda x: np.asarray(x, dtype=np.float32).astype(np.float64))
+    with pytest.raises(AssertionError):
+        test_fp8_dequant_definition()
+    with pytest.raises(AssertionError):
+        test_fp8_rows_match_torch_dequant()
 
 
 def test_pins_catch_dropped_rope_term(monkeypatch):
