@@ -371,6 +371,35 @@ def test_split_items_at_several_worker_counts(W):
     compare(o.cpu().numpy(), l.cpu().numpy(), ro, rl, BF16_TOL, f"splits W={W}")
 
 
+@pytest.mark.parametrize("W", [600, 4096])
+def test_more_workers_than_compute_units(W):
+    """A grid larger than the chip (several work-groups per CU over time, the planner's maximum of
+    4,096 workers): long and short sequences cut into many small runs; every output."""
+    w = wl.make_workload("wide-grid", batch=5, s_q=2, heads=64, seqlens=[30000, 9000, 700, 65, 2], causal=True,
+                         seed=46)
+    _say("workers", W)
+    _check_full(w, num_workers=W, what=f"workers={W}")
+
+
+def test_most_items():
+    """The largest plan: 16,384 items (16,384 sequences of one 16-row tile), lengths 0..150 drawn
+    per sequence, 256 workers; every output."""
+    lens = np.random.default_rng(47).integers(0, 151, 16384)
+    w = wl.make_workload("most-items", batch=16384, s_q=1, heads=16, seqlens=lens, seed=47)
+    _say("most items")
+    _check_full(w, num_workers=256, what="16384 items")
+
+
+def test_widest_block_table():
+    """max_pages = 65,535 (the largest block-table row): the table's row stride is taken from
+    max_pages, not from the lengths."""
+    w = wl.make_workload("wide-table", batch=3, s_q=1, heads=32, seqlens=[5000, 64, 700], seed=48,
+                         max_pages=65535)
+    assert w.block_table.shape == (3, 65535)
+    _say("widest block table")
+    _check_full(w, num_workers=32, what="max_pages=65535")
+
+
 def test_plan_reused_across_calls():
     """One plan serves many calls (as one plan serves every layer of a decode step): five calls,
     outputs NaN before each, all bitwise equal and matching the oracle."""
