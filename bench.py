@@ -506,8 +506,8 @@ def main():
         "arith_intensity": round(ai, 1),
         "roofline_bound_us": round(bound_us, 2),
         "roofline_frac_of_bound": round(bound_us / dec_mean, 4),
-        "roofline": dict(roof, kernel="mla_decode_fwd (decode kernel with its split merge, and the combine "
-                                      "kernel for wide splits)", bytes_per_call=byts, flops_per_call=flops),
+        "roofline": dict(roof, kernel="mla_decode_fwd: decode_rows32_kernel, then combine_rows32_kernel (the "
+                                      "merge of split items)", bytes_per_call=byts, flops_per_call=flops),
     }
     if w.kv_dtype == "bf16" and not args.no_projections:
         rec["projections"] = projections(w, args.steps, min(args.warmup, 50))
