@@ -112,6 +112,10 @@ __device__ __forceinline__ uint32_t dma_voff(const DmaOffsets& d, int n) {
 __device__ __forceinline__ void issue32(const i32x4& rsrc, uint32_t lds_slot, int n, uint32_t voff, int wave) {
   lds_dma_x4(lds_slot + 1024u * (uint32_t)(wave + 4 * n), voff, rsrc);
 }
+// the same for cache rows (read once: non-temporal)
+__device__ __forceinline__ void issue32_rows(const i32x4& rsrc, uint32_t lds_slot, int n, uint32_t voff, int wave) {
+  lds_dma_x4_stream(lds_slot + 1024u * (uint32_t)(wave + 4 * n), voff, rsrc);
+}
 
 // fp8 staging slot of one step, filled by 21 LDS-DMA instructions:
 //  * codes: token u's 512 codes at 512u, its 32-B pieces (32 channels) permuted within each
@@ -394,17 +398,17 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     if constexpr (kSparse) {
       const uint32_t none = 0xFFFFFFF0u;
       if (j < 4) {
-        lds_dma_x4(st + 1024u * (uint32_t)(wave + 4 * j), sv ? (sv - 1u) * kF8Row + (f8_dma & 0xFFFFu) : none, rs.kv);
+        lds_dma_x4_stream(st + 1024u * (uint32_t)(wave + 4 * j), sv ? (sv - 1u) * kF8Row + (f8_dma & 0xFFFFu) : none, rs.kv);
       } else if (j == 4) {
-        lds_dma_x4(st + kR8StRope + 1024u * (uint32_t)wave, sv ? (sv - 1u) * kF8Row + (f8_dma >> 16) : none, rs.kv);
+        lds_dma_x4_stream(st + kR8StRope + 1024u * (uint32_t)wave, sv ? (sv - 1u) * kF8Row + (f8_dma >> 16) : none, rs.kv);
       } else if (wave == 0) {
         lds_dma_x4(st + kR8StScales, (sv && lane < 32) ? (sv - 1u) * 16u : none, rs.sc);
       }
     } else {
       if (j < 4) {
-        lds_dma_x4(st + 1024u * (uint32_t)(wave + 4 * j), (f8_dma & 0xFFFFu) + 8u * kF8Row * (uint32_t)j, rs.kv);
+        lds_dma_x4_stream(st + 1024u * (uint32_t)(wave + 4 * j), (f8_dma & 0xFFFFu) + 8u * kF8Row * (uint32_t)j, rs.kv);
       } else if (j == 4) {
-        lds_dma_x4(st + kR8StRope + 1024u * (uint32_t)wave, f8_dma >> 16, rs.kv);
+        lds_dma_x4_stream(st + kR8StRope + 1024u * (uint32_t)wave, f8_dma >> 16, rs.kv);
       } else if (wave == 0) {
         lds_dma_x4(st + kR8StScales, lane < 32 ? 16u * (uint32_t)lane : 0x40000000u, rs.sc);
       }
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
       for (int j = 0; j < 6; ++j) dma_f8(rs, st, j, kSparse ? f8_row(j) : 0u);
     } else {
 #pragma unroll
-      for (int n = 0; n < kR32Dma; ++n) issue32(rs.kv, lds_u32 + load_slot * kBufBytes, n, dma_voff(dmo, n), wave);
+      for (int n = 0; n < kR32Dma; ++n) issue32_rows(rs.kv, lds_u32 + load_slot * kBufBytes, n, dma_voff(dmo, n), wave);
     }
     advance();
   };
@@ -896,7 +900,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
             if (t == 0) mfma_v0(s, cur, qreg[0]);
             else mfma_v(s, cur, qreg[t]);
             if ((t & 3) == 0) voff = dma_voff(dmo, t >> 2);   // offset of the next DMA instruction
-            if ((t & 3) == 3) issue32(rs.kv, lslot, t >> 2, voff, wave);
+            if ((t & 3) == 3) issue32_rows(rs.kv, lslot, t >> 2, voff, wave);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
