@@ -77,13 +77,27 @@ def traffic_from_profile(kernel_srcs, key):
     return rec.get(key, {}).get("bytes_per_call")
 
 
+def _events_us(stream, fn, n: int) -> float:
+    """Mean µs per call of fn(i), i < n, from one pair of HIP events on `stream` around n
+    back-to-back calls (a pair per call would add its own gaps between the calls)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
 def projections(w, steps: int, warmup: int, copies: int = 16):
     """The two projections around the attention at this workload's shape (tokens = b*s, h
-    heads), each timed with HIP events over `steps` calls on the launch stream, cycling
-    through `copies` sets of weights (more than the 256 MB Infinity Cache holds) with
-    seeded random values: query absorption (mla_absorb_query) and output decompression
-    (mla_decompress_output). Bytes are the algorithmic reads and writes of one call."""
-    import numpy as np
+    heads), each timed with one pair of HIP events on the launch stream around `steps`
+    back-to-back calls, cycling through `copies` sets of weights (more than the 256 MB
+    Infinity Cache holds) with seeded random values: query absorption (mla_absorb_query) and
+    output decompression (mla_decompress_output). Bytes are the algorithmic reads and writes
+    of one call."""
     import torch
     import mla_latent_space_amd as mla
     dev = "cuda"
@@ -107,14 +121,7 @@ def projections(w, steps: int, warmup: int, copies: int = 16):
     for name, (fn, byts) in calls.items():
         for i in range(warmup):
             fn(i)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        torch.cuda.synchronize()
-        for i in range(steps):
-            ev[i][0].record(stream)
-            fn(i)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        us = _events_us(stream, fn, steps)
         gbps = byts / (us * 1e-6) / 1e9
         res[name] = {"us": round(us, 2), "bytes": byts, "flops": 2 * T * H * 512 * 128,
                      "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -131,7 +138,6 @@ def hybrid(steps: int, warmup: int, b: int = 32, s_q: int = 16, heads: int = 128
     causal decode over t tokens, decompression). n = 640 is where the cost model balances the
     MFMA time of the latent tokens against the HBM time of the decompressed ones on MI355X.
     Seeded random inputs generated on the device; two copies of every cache are cycled."""
-    import numpy as np
     import torch
     import mla_latent_space_amd as mla
     dev = "cuda"
@@ -190,15 +196,9 @@ def hybrid(steps: int, warmup: int, b: int = 32, s_q: int = 16, heads: int = 128
         return (time.perf_counter() - t0) / steps * 1e6
 
     hyb_us, lat_us = wall_us(hybrid_step), wall_us(latent_step)
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        latent_part(i, kv_old, bt_old, sl_old, False)
-        ev[i][0].record(stream)
-        merge(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    merge_us = float(np.mean([a.elapsed_time(c) * 1e3 for a, c in ev]))
+    # the merge alone: back-to-back calls on the latent part of the last step
+    latent_part(0, kv_old, bt_old, sl_old, False)
+    merge_us = _events_us(torch.cuda.current_stream(), merge, steps)
     rows = b * s_q * heads
     merge_bytes = b * n * heads * 128 * 2 * 2 + b * n * 64 * 2 + rows * ((128 + 64) * 2 + 2 * 128 * 4 + 2 * 4)
     merge_flops = 4.0 * b * heads * s_q * n * 128 + 2.0 * b * heads * s_q * n * 64
@@ -225,7 +225,6 @@ def sparse(steps: int, warmup: int, b: int = 64, t: int = 32768, topk: int = 204
     tokens (a seeded uniform choice without replacement, in random order). One step = the row
     lists and split plan (mla_get_sparse_plan) and the decode (mla_sparse_decode_fwd). Seeded
     random codes (NaN codes excluded), scales and rope values generated on the device."""
-    import numpy as np
     import torch
     import mla_latent_space_amd as mla
     dev = "cuda"
@@ -262,14 +261,9 @@ def sparse(steps: int, warmup: int, b: int = 64, t: int = 32768, topk: int = 204
         step(i)
     torch.cuda.synchronize()
     step_us = (time.perf_counter() - t0) / steps * 1e6
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        mla.sparse_decode_fwd(q, kv, scales, scale, plan, workspace=ws, out=out, lse=lse)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    dec_us = float(np.mean([a.elapsed_time(c) * 1e3 for a, c in ev]))
+    dec_us = _events_us(torch.cuda.current_stream(),
+                        lambda i: mla.sparse_decode_fwd(q, kv, scales, scale, plan, workspace=ws, out=out, lse=lse),
+                        max(steps, 200))
     rows = b * heads
     byts = float(b * topk * (512 + 128 + 16) + b * topk * 4 + rows * 576 * 2 + rows * (512 + 1) * 4)
     flops = 2.0 * rows * topk * (2 * K_LAT + P_ROPE)
