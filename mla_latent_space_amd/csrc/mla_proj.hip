@@ -11,7 +11,9 @@
 // chunks of 128: the chunk's operand blocks are copied into LDS by LDS-DMA (1 KiB contiguous
 // per instruction; loaded straight into MFMA fragments, every load instruction would touch
 // 32 rows), 16-byte chunks XOR-swizzled by row so that the fragment reads (32 rows x one
-// chunk) are free of bank conflicts, then 8 MFMAs per wave. Rows past the last token read as
+// chunk) are free of bank conflicts, then 8 MFMAs per wave. With more than one chunk (the
+// decompression, k = 512) the blocks are double-buffered: chunk c+1 loads while chunk c is
+// multiplied. Rows past the last token read as
 // zeros (buffer range check). The decode's fp32 O_latent is rounded to bf16 when read.
 #include "mla_device.h"
 
@@ -39,9 +41,16 @@ __device__ __forceinline__ void stage_block(const i32x4& rsrc, uint32_t lds_dst,
   }
 }
 
+// DMA instructions one wave issues for one chunk (B block, then A block)
+template <bool kAFloat>
+constexpr int chunk_dma_per_wave() {
+  return (128 * kProjKc * 2 / 16 / 64 + 32 * kProjKc * (kAFloat ? 4 : 2) / 16 / 64) / 4;
+}
+
 // C[t, h, n] = sum_k A[t, h, k] B[h, n, k] for n < N (A rows of K elements, C rows of ldc
-// elements); with a rope operand, C[t, h, N .. N+63] = rope[t, h, 0 .. 63] as well.
-template <bool kAFloat, bool kCBf16>
+// elements); with a rope operand, C[t, h, N .. N+63] = rope[t, h, 0 .. 63] as well. kDb: two
+// LDS buffers (K > kProjKc).
+template <bool kAFloat, bool kCBf16, bool kDb>
 __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restrict__ A, const __bf16* __restrict__ B,
                                                             void* __restrict__ C, const __bf16* __restrict__ rope,
                                                             int T, int H, int K, int N, int ldc) {
@@ -56,39 +65,54 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
   const i32x4 ra = make_rsrc(reinterpret_cast<uint64_t>(A), (int)((int64_t)T * H * K * esz));
   // B: rows nb .. nb+127 of head h, K elements each
   const i32x4 rb = make_rsrc(reinterpret_cast<uint64_t>(B) + ((uint64_t)h * N + nb) * K * 2, 128 * K * 2);
-  const uint32_t a_lds = lds_u32 + kProjBBytes;
+  constexpr uint32_t kBufBytesP = kProjBBytes + 32 * a_row_bytes;   // one buffer: B block, then A block
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   const int l32 = lane & 31, hh = lane >> 5;
   const int nrow = 32 * wave + l32;   // this lane's row of the B block
+  auto stage = [&](int kc, uint32_t buf) {
+    stage_block(rb, lds_u32 + buf, (uint32_t)kc * 2, (uint32_t)K * 2, 128, 2, tid);
+    stage_block(ra, lds_u32 + buf + kProjBBytes, (uint32_t)(((int64_t)m0 * H + h) * K + kc) * esz,
+                (uint32_t)H * K * esz, 32, esz, tid);
+  };
+  if (kDb) stage(0, 0u);
   for (int kc = 0; kc < K; kc += kProjKc) {
-    stage_block(rb, lds_u32, (uint32_t)kc * 2, (uint32_t)K * 2, 128, 2, tid);
-    stage_block(ra, a_lds, (uint32_t)(((int64_t)m0 * H + h) * K + kc) * esz, (uint32_t)H * K * esz, 32, esz, tid);
-    wait_vmcnt<0>();
+    const uint32_t buf = kDb ? ((kc / kProjKc) & 1) * kBufBytesP : 0u;
+    if (kDb) {
+      if (kc + kProjKc < K) {
+        stage(kc + kProjKc, kBufBytesP - buf);   // the next chunk into the other buffer
+        wait_vmcnt<chunk_dma_per_wave<kAFloat>()>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    } else {
+      stage(kc, 0u);
+      wait_vmcnt<0>();
+    }
     barrier_lds();
 #pragma unroll
     for (int j = 0; j < kProjKc / 16; ++j) {
       const int c = 2 * j + hh;   // logical 16-B chunk of k 16j + 8hh .. +7 (bf16)
-      const bf16x8 bf = lds_b128(lds + (nrow * 256 + 16 * (c ^ (nrow & 15))));
+      const bf16x8 bf = lds_b128(lds + (buf + nrow * 256 + 16 * (c ^ (nrow & 15))));
       bf16x8 af;
       if (kAFloat) {
         // fp32: the 8 values are logical chunks 2c, 2c+1 of a 512-B row
-        const f32x4 lo = *(const f32x4 __attribute__((address_space(3)))*)(lds + (kProjBBytes + l32 * a_row_bytes +
-                                                                                    16 * ((2 * c) ^ (l32 & 15))));
-        const f32x4 hi = *(const f32x4 __attribute__((address_space(3)))*)(lds + (kProjBBytes + l32 * a_row_bytes +
-                                                                                    16 * ((2 * c + 1) ^ (l32 & 15))));
+        const f32x4 lo = *(const f32x4 __attribute__((address_space(3)))*)(
+            lds + (buf + kProjBBytes + l32 * a_row_bytes + 16 * ((2 * c) ^ (l32 & 15))));
+        const f32x4 hi = *(const f32x4 __attribute__((address_space(3)))*)(
+            lds + (buf + kProjBBytes + l32 * a_row_bytes + 16 * ((2 * c + 1) ^ (l32 & 15))));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           af[i] = (__bf16)lo[i];
           af[4 + i] = (__bf16)hi[i];
         }
       } else {
-        af = lds_b128(lds + (kProjBBytes + l32 * a_row_bytes + 16 * (c ^ (l32 & 15))));
+        af = lds_b128(lds + (buf + kProjBBytes + l32 * a_row_bytes + 16 * (c ^ (l32 & 15))));
       }
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
     }
-    barrier_lds();   // the blocks are read before the next chunk overwrites them
+    barrier_lds();   // the blocks are read before a later chunk overwrites them
   }
   const int n0 = nb + 32 * wave;
   // acc register r of lane l: row m0 + 8(r/4) + 4(l/32) + r%4, column n0 + l%32
@@ -112,14 +136,17 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
   }
 }
 
-constexpr int proj_lds_bytes(bool a_float) { return kProjBBytes + 32 * kProjKc * (a_float ? 4 : 2); }
+constexpr int proj_lds_bytes(bool a_float, bool db) {
+  return (db ? 2 : 1) * (kProjBBytes + 32 * kProjKc * (a_float ? 4 : 2));
+}
 
 }  // namespace
 
 hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int tokens, int heads,
                                void* qz, hipStream_t stream) {
   const dim3 grid(kLat / 128, (tokens + 31) / 32, heads);
-  hipLaunchKernelGGL((proj_kernel<false, true>), grid, dim3(kProjThreads), proj_lds_bytes(false), stream, q_nope,
+  hipLaunchKernelGGL((proj_kernel<false, true, false>), grid, dim3(kProjThreads), proj_lds_bytes(false, false), stream,
+                     q_nope,
                      static_cast<const __bf16*>(w_k), qz, static_cast<const __bf16*>(q_rope), tokens, heads,
                      kNope, kLat, kDqk);
   return hipGetLastError();
@@ -127,8 +154,18 @@ hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const voi
 
 hipError_t launch_decompress_output(const float* out_latent, const void* w_v, int tokens, int heads, float* out,
                                     hipStream_t stream) {
+  static thread_local int configured = -1;   // the LDS opt-in (96 KiB, two buffers) is per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (configured != dev) {
+    e = hipFuncSetAttribute((const void*)proj_kernel<true, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            proj_lds_bytes(true, true));
+    if (e != hipSuccess) return e;
+    configured = dev;
+  }
   const dim3 grid(1, (tokens + 31) / 32, heads);
-  hipLaunchKernelGGL((proj_kernel<true, false>), grid, dim3(kProjThreads), proj_lds_bytes(true), stream,
+  hipLaunchKernelGGL((proj_kernel<true, false, true>), grid, dim3(kProjThreads), proj_lds_bytes(true, true), stream,
                      static_cast<const void*>(out_latent), static_cast<const __bf16*>(w_v), static_cast<void*>(out),
                      static_cast<const __bf16*>(nullptr), tokens, heads, kLat, kDv, kDv);
   return hipGetLastError();
