@@ -655,6 +655,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     // on every step of a tracking pass. Elsewhere the only guard is the row sum: it bounds
     // every P, and the pass ends with a check that it stayed below 2^60.
     float sm_mx, sm_muse = 0.f, sm_psum;
+    float sm_x = 0.f, sm_e = 0.f;   // skewed exp stages
     bool sm_do_max = true, sm_masked = false, track = false;
     auto softmax_piece = [&](f32x16& s, int hh, bool live, int piece, bf16x8* pk) {
       if (piece == 0) {
@@ -690,17 +691,22 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
           sm_muse = (m_run == -INFINITY) ? 0.f : m_run;
         }
         sm_psum = 0.f;
-      } else if (piece <= 21) {
-        const int r = piece - 6;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -sm_muse));
-        sm_psum += p;
-        pk[r >> 3][r & 7] = (__bf16)p;
+      } else if (piece <= 23) {
+        // three stages a piece apart (scaled logit of element k - 6, its exponential at
+        // k - 7, sum and bf16 at k - 8), so that no piece is one dependent chain
+        const int rf = piece - 6, re = piece - 7, ra = piece - 8;
+        if (ra >= 0 && ra < 16) {
+          sm_psum += sm_e;
+          pk[ra >> 3][ra & 7] = (__bf16)sm_e;
+        }
+        if (re >= 0 && re < 16) sm_e = __builtin_amdgcn_exp2f(sm_x);
+        if (rf < 16) sm_x = __builtin_fmaf(s[rf], a.scale_log2, -sm_muse);
       } else {
         const float psum = sum_across_halves(sm_psum);
         l_run = live ? l_run + psum : l_run;
       }
     };
-    constexpr int kPieces = 23;
+    constexpr int kPieces = 25;
     // this wave's P tiles (k-steps 0, 1) into P buffer b: tile (row block, k-step q) is 1 KiB
     // at (2 row block + q) KiB, 16 B per lane, the A-operand layout
     auto p_store = [&](int b, const bf16x8* pk) {
@@ -929,19 +935,16 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
             // one softmax piece after each value MFMA
             const int u = t - kR32PvLead;
             if (u < kPieces) softmax_piece(s, sg.hh0 + i + 1, live, u, pnext);
+            // the first value operands of step i+1 once this step's k-step-0 MFMAs are done
+            // (its rows were published at the last barrier), and the P of step i+1 once the
+            // softmax has formed it, so that their LDS latency ends before the barrier
+            if (t >= 17 && t <= 23 && (t & 1)) bq0[(t - 17) >> 1] = pv_read(pv_at(pv0, zn), (t - 17) >> 1);
+            if (t == 29) p_store((i + 1) & 1, pnext);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        // P of step i+1 for this wave's rows to the other P buffer (published by the barrier)
-        p_store((i + 1) & 1, pnext);
         pcur[0] = pnext[0];
         pcur[1] = pnext[1];
-        // the first value operands of step i+1 (its rows were published at the last barrier)
-        {
-          const PvAddr pa = pv_at(pv0, zn);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) bq0[c] = pv_read(pa, c);
-        }
         }
         // move the load cursor here: its scalar loads share the LDS counter, and the barrier
         // waits for that counter anyway
