@@ -7,7 +7,11 @@
 //    (one row of 512 coefficients per output channel, the usual linear-layer layout); the
 //    page leaves this to a separate kernel after the attention.
 // In both, the contraction index is the innermost one of both operands. One work-group per
-// (128 output columns, 32 rows, head); wave w takes columns 32w .. 32w+31. The k loop runs in
+// (128 output columns, 32 rows, head); wave w takes columns 32w .. 32w+31. The 1-D grid puts
+// the token tiles of one (head, column tile), which read the same weight block, on one XCD
+// (work-groups are dealt to the 8 XCDs by block index), so that the block comes from HBM once
+// and from that XCD's L2 after: 10.1 -> 8.3 us (absorption) and 9.2 -> 7.9 us
+// (decompression) at 64 tokens x 128 heads. The k loop runs in
 // chunks of 128: the chunk's operand blocks are copied into LDS by LDS-DMA (1 KiB contiguous
 // per instruction; loaded straight into MFMA fragments, every load instruction would touch
 // 32 rows), 16-byte chunks XOR-swizzled by row so that the fragment reads (32 rows x one
@@ -60,7 +64,13 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
   constexpr int esz = kAFloat ? 4 : 2;
   constexpr int a_row_bytes = kProjKc * esz;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.z, m0 = 32 * blockIdx.y, nb = 128 * blockIdx.x;
+  // block -> (column tile, token tile, head): the token tiles of one (head, column tile), which read
+  // the same weight block, share a block-index residue mod 8 and so an XCD and its L2
+  const int ncol = N / 128, ntile = (T + 31) / 32;
+  const int lin = blockIdx.x, x8 = lin & 7, r = lin >> 3;
+  const int ytile = r % ntile, pair = (r / ntile) * 8 + x8;
+  if (pair >= ncol * H) return;
+  const int h = pair / ncol, m0 = 32 * ytile, nb = 128 * (pair - h * ncol);
   // A: all T rows of head h; row m at byte (m H + h) K esz; the range check zero-fills m >= T
   const i32x4 ra = make_rsrc(reinterpret_cast<uint64_t>(A), (int)((int64_t)T * H * K * esz));
   // B: rows nb .. nb+127 of head h, K elements each
@@ -124,7 +134,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
     if (kCBf16) static_cast<__bf16*>(C)[ci] = (__bf16)acc[r];
     else static_cast<float*>(C)[ci] = acc[r];
   }
-  if (rope != nullptr && blockIdx.x == 0) {
+  if (rope != nullptr && nb == 0) {
     // 32 rows x 64 rope values (128 B per row): one 16-B chunk per thread
     const int rr = tid >> 3, ch = tid & 7;
     const int m = m0 + rr;
@@ -144,7 +154,8 @@ constexpr int proj_lds_bytes(bool a_float, bool db) {
 
 hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int tokens, int heads,
                                void* qz, hipStream_t stream) {
-  const dim3 grid(kLat / 128, (tokens + 31) / 32, heads);
+  const int pairs = (kLat / 128) * heads;
+  const dim3 grid(((pairs + 7) / 8) * 8 * ((tokens + 31) / 32));
   hipLaunchKernelGGL((proj_kernel<false, true, false>), grid, dim3(kProjThreads), proj_lds_bytes(false, false), stream,
                      q_nope,
                      static_cast<const __bf16*>(w_k), qz, static_cast<const __bf16*>(q_rope), tokens, heads,
@@ -164,7 +175,8 @@ hipError_t launch_decompress_output(const float* out_latent, const void* w_v, in
     if (e != hipSuccess) return e;
     configured = dev;
   }
-  const dim3 grid(1, (tokens + 31) / 32, heads);
+  const int pairs = heads;
+  const dim3 grid(((pairs + 7) / 8) * 8 * ((tokens + 31) / 32));
   hipLaunchKernelGGL((proj_kernel<true, false, true>), grid, dim3(kProjThreads), proj_lds_bytes(true, true), stream,
                      static_cast<const void*>(out_latent), static_cast<const __bf16*>(w_v), static_cast<void*>(out),
                      static_cast<const __bf16*>(nullptr), tokens, heads, kLat, kDv, kDv);
