@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import mla_latent_space_amd as mla
 
@@ -180,3 +181,165 @@ def test_sparse_calls_reject_bad_arguments_before_launch():
     assert dec(scale=-1.0) == 1
     assert dec(ws_bytes=16) == 3
     assert dec(out=f + 8) == 1
+
+
+# ----------------------------------------------------------------------------- Python binding
+# The binding checks every tensor's shape, dtype and layout before it looks at devices, so these
+# run on CPU tensors: each wrong argument raises ValueError naming the tensor and the fault, and a
+# call whose shapes are all right stops at the device check (nothing is enqueued on CPU).
+
+
+def _decode_inputs(batch=2, s_q=1, heads=16, pages=6, max_pages=4, W=4, fp8=False, causal=False):
+    width = 640 if fp8 else 576
+    kv = torch.zeros(pages, 64, width, dtype=torch.uint8 if fp8 else torch.bfloat16)
+    ok = dict(q=torch.zeros(batch, s_q, heads, 576, dtype=torch.bfloat16), kv_cache=kv,
+              block_table=torch.zeros(batch, max_pages, dtype=torch.int32),
+              seqlens=torch.zeros(batch, dtype=torch.int32), softmax_scale=0.07, causal=causal,
+              plan=mla.SplitPlan(torch.zeros(mla.plan_bytes(batch, s_q, heads, W), dtype=torch.uint8), batch, s_q,
+                                 heads, causal, W))
+    if fp8:
+        ok["kv_scales"] = torch.ones(pages, 64, 4)
+    return ok
+
+
+def test_binding_rejects_wrong_decode_arguments():
+    batch, s_q, heads, W = 2, 1, 16, 4
+    ok = _decode_inputs(batch, s_q, heads, W=W)
+    wide_q = torch.zeros(batch, s_q, heads, 1152, dtype=torch.bfloat16)
+    cases = [
+        (dict(q=ok["q"][..., :512]), r"q must be \[batch, s_q, heads, 576\]"),
+        (dict(q=ok["q"][0]), r"q must be \[batch"),
+        (dict(q=ok["q"].float()), "q must have dtype"),
+        (dict(q=wide_q[..., :576]), "q must be contiguous"),
+        (dict(kv_cache=ok["kv_cache"].view(-1, 576)), r"kv_cache must be \[pages, 64, 576\]"),
+        (dict(kv_cache=ok["kv_cache"].view(-1, 32, 1152)), "kv_cache must have shape"),
+        (dict(kv_cache=ok["kv_cache"].float()), "kv_cache must be bfloat16"),
+        (dict(kv_scales=torch.ones(6, 64, 4)), "kv_scales must be None"),
+        (dict(block_table=ok["block_table"][:1]), "block_table must have shape"),
+        (dict(block_table=ok["block_table"].flatten()), r"block_table must be \[batch, max_pages\]"),
+        (dict(block_table=ok["block_table"].long()), "block_table must have dtype"),
+        (dict(seqlens=torch.zeros(batch + 1, dtype=torch.int32)), "seqlens must have shape"),
+        (dict(seqlens=ok["seqlens"].long()), "seqlens must have dtype"),
+        (dict(plan=mla.SplitPlan(ok["plan"].buffer, batch, s_q, 32, False, W)), "plan was built for different"),
+        (dict(causal=True), "plan was built for different"),
+        (dict(plan=mla.SplitPlan(ok["plan"].buffer[:64], batch, s_q, heads, False, W)), "plan buffer must be"),
+        (dict(out=torch.zeros(batch, s_q, heads, 128)), "out must have shape"),
+        (dict(out=torch.zeros(batch, s_q, heads, 512, dtype=torch.float64)), "out must have dtype"),
+        (dict(lse=torch.zeros(batch, s_q, heads, 1)), "lse must have shape"),
+        (dict(lse=torch.zeros(batch, s_q, heads, dtype=torch.float64)), "lse must have dtype"),
+        (dict(workspace=torch.zeros(16, dtype=torch.uint8)), "workspace must be"),
+        (dict(status=torch.zeros(1, dtype=torch.int64)), "status must be"),
+        (dict(status=torch.zeros(0, dtype=torch.int32)), "status must be"),
+    ]
+    for kw, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            mla.decode_fwd(**{**ok, **kw})
+    # the no-allocation entry point goes through the same checks (no workspace argument)
+    for kw, msg in cases:
+        if "workspace" not in kw:
+            with pytest.raises(ValueError, match=msg):
+                mla.decode_fwd_noalloc(**{**ok, **kw})
+    # right shapes everywhere: the only fault left is that the tensors are not on a GPU
+    with pytest.raises(ValueError, match="CUDA"):
+        mla.decode_fwd(**ok)
+    with pytest.raises(ValueError, match="CUDA"):
+        mla.decode_fwd_noalloc(**ok)
+
+
+def test_binding_rejects_wrong_fp8_decode_arguments():
+    ok = _decode_inputs(fp8=True)
+    cases = [
+        (dict(kv_scales=None), "kv_scales float32 .* is required"),
+        (dict(kv_scales=torch.ones(6, 64, 2)), "kv_scales must have shape"),
+        (dict(kv_scales=torch.ones(5, 64, 4)), "kv_scales must have shape"),
+        (dict(kv_scales=torch.ones(6, 64, 4, dtype=torch.float64)), "kv_scales must have dtype"),
+        (dict(kv_cache=torch.zeros(6, 64, 576, dtype=torch.uint8)), "kv_cache must have shape"),
+    ]
+    for kw, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            mla.decode_fwd(**{**ok, **kw})
+    with pytest.raises(ValueError, match="CUDA"):
+        mla.decode_fwd(**ok)
+    with pytest.raises(ValueError, match="CUDA"):
+        mla.decode_fwd(**{**ok, "kv_cache": ok["kv_cache"].view(torch.float8_e4m3fn)})
+
+
+def test_binding_rejects_wrong_plan_and_projection_arguments():
+    with pytest.raises(ValueError, match=r"seqlens must be \[batch\]"):
+        mla.get_split_plan(torch.zeros(2, 1, dtype=torch.int32), 1, 128)
+    with pytest.raises(ValueError, match="seqlens must have dtype"):
+        mla.get_split_plan(torch.zeros(2, dtype=torch.int64), 1, 128)
+    with pytest.raises(ValueError, match="CUDA"):
+        mla.get_split_plan(torch.zeros(2, dtype=torch.int32), 1, 128, num_workers=8)
+
+    b, s, h = 2, 3, 16
+    qn = torch.zeros(b, s, h, 128, dtype=torch.bfloat16)
+    qr = torch.zeros(b, s, h, 64, dtype=torch.bfloat16)
+    wk = torch.zeros(h, 512, 128, dtype=torch.bfloat16)
+    for args, msg in [((qn, qr[..., :32], wk), "q_rope must have shape"),
+                      ((qn, qr, wk.transpose(1, 2)), "w_k must have shape"),
+                      ((qn, qr, torch.zeros(h, 512, 128)), "w_k must have dtype"),
+                      ((qn[0, 0, 0], qr, wk), r"q_nope must be \[\.\.\., heads, 128\]"),
+                      ((qn, qr, wk, torch.zeros(b, s, h, 576)), "out must have dtype"),
+                      ((qn, qr, wk), "CUDA")]:
+        with pytest.raises(ValueError, match=msg):
+            mla.absorb_query(*args)
+    ol = torch.zeros(b, s, h, 512)
+    wv = torch.zeros(h, 128, 512, dtype=torch.bfloat16)
+    for args, msg in [((ol.bfloat16(), wv), "out_latent must have dtype"),
+                      ((ol, wv[:, :64]), "w_v must have shape"),
+                      ((ol, wv, torch.zeros(b, s, h, 512)), "out must have shape"),
+                      ((ol, wv), "CUDA")]:
+        with pytest.raises(ValueError, match=msg):
+            mla.decompress_output(*args)
+
+
+def test_binding_rejects_wrong_hybrid_and_sparse_arguments():
+    b, s, h, n = 2, 3, 16, 40
+    qn = torch.zeros(b, s, h, 128, dtype=torch.bfloat16)
+    qr = torch.zeros(b, s, h, 64, dtype=torch.bfloat16)
+    kn = torch.zeros(b, n, h, 128, dtype=torch.bfloat16)
+    krn = torch.zeros(b, n, 64, dtype=torch.bfloat16)
+    oo = torch.zeros(b, s, h, 128)
+    lo = torch.zeros(b, s, h)
+    ok = dict(q_nope=qn, q_rope=qr, k_new=kn, kr_new=krn, v_new=kn.clone(), out_old=oo, lse_old=lo,
+              softmax_scale=0.1)
+    for kw, msg in [(dict(kr_new=torch.zeros(b, n, h, 64, dtype=torch.bfloat16)), "kr_new must have shape"),
+                    (dict(v_new=kn[:, :-1]), "v_new must have shape"),
+                    (dict(k_new=kn[0]), r"k_new must be \[batch, n_new, heads, 128\]"),
+                    (dict(lse_old=lo.double()), "lse_old must have dtype"),
+                    (dict(out_old=oo[:1]), "out_old must have shape"),
+                    (dict(out=torch.zeros(b, s, h, 512)), "out must have shape"),
+                    (dict(q_nope=qn[0]), r"q_nope must be \[batch"),
+                    (dict(), "CUDA"),
+                    (dict(k_new=None, kr_new=None, v_new=None), "CUDA")]:
+        with pytest.raises(ValueError, match=msg):
+            mla.hybrid_merge(**{**ok, **kw})
+
+    idx = torch.zeros(b, 1, 64, dtype=torch.int32)
+    bt = torch.zeros(b, 4, dtype=torch.int32)
+    sl = torch.zeros(b, dtype=torch.int32)
+    for args, msg in [((idx[0], bt, sl, 10), r"indices must be \[batch, s_q, topk\]"),
+                      ((idx.long(), bt, sl, 10), "indices must have dtype"),
+                      ((idx, bt[:1], sl, 10), "block_table must have shape"),
+                      ((idx, bt, sl[:1], 10), "seqlens must have shape"),
+                      ((idx, bt, sl, 10), "CUDA")]:
+        with pytest.raises(ValueError, match=msg):
+            mla.get_sparse_plan(*args, num_workers=8)
+
+    pages, W = 10, 8
+    plan = mla.SparsePlan(torch.zeros(64, dtype=torch.uint8), torch.zeros(64, dtype=torch.uint8), b, 1, 128, 64,
+                          pages, W)
+    q = torch.zeros(b, 1, 128, 576, dtype=torch.bfloat16)
+    kv = torch.zeros(pages, 64, 640, dtype=torch.uint8)
+    sc = torch.ones(pages, 64, 4)
+    for kw, msg in [(dict(kv_scales=sc[:, :, :2]), "kv_scales must have shape"),
+                    (dict(kv_scales=sc[:5]), "kv_scales must have shape"),
+                    (dict(kv_cache=kv[:5]), "kv_cache .* must have shape"),
+                    (dict(kv_cache=torch.zeros(pages, 64, 576, dtype=torch.bfloat16)), "kv_cache .* must have shape"),
+                    (dict(q=q[:, :, :64]), "q must have shape"),
+                    (dict(workspace=torch.zeros(16, dtype=torch.uint8)), "workspace must be"),
+                    (dict(lse=torch.zeros(b, 1, 128, dtype=torch.float16)), "lse must have dtype"),
+                    (dict(), "CUDA")]:
+        with pytest.raises(ValueError, match=msg):
+            mla.sparse_decode_fwd(**{**dict(q=q, kv_cache=kv, kv_scales=sc, softmax_scale=0.1, plan=plan), **kw})
