@@ -33,8 +33,7 @@
  *    0 <= seqlens[i] <= max_pages * 64 and block_table[i, r] in [0, num_pages) for
  *    r < ceil(seqlens[i] / 64), and a plan built for the call's arguments. The kernels never
  *    fault on a violation: a page id outside [0, num_pages) reads as zeros, a length above
- *    max_pages * 64 reads only max_pages pages, and a mismatched plan (in a buffer of at least
- *    mla_plan_bytes for the call's arguments, as every plan argument must be) writes no output. Each
+ *    max_pages * 64 reads only max_pages pages, and a mismatched plan writes no output. Each
  *    violation sets a bit (MLA_DEVICE_*) in the call's optional device status word, and with
  *    the environment variable MLA_VALIDATE=1 the call synchronises its stream after the launch
  *    and returns MLA_ERR_INVALID_ARG naming the violations (not under stream capture).
@@ -140,10 +139,7 @@ int32_t mla_get_split_plan(const int32_t* seqlens, int32_t batch, int32_t s_q, i
  * seqlens     device int32 [batch] (same contents as given to the plan).
  * batch, s_q, heads, causal   as for mla_get_split_plan (must match the plan).
  * softmax_scale  multiplies every score (e.g. 1/sqrt(192)); finite and > 0.
- * plan        device plan from mla_get_split_plan for the same arguments, in its buffer of at
- *             least mla_plan_bytes(batch, s_q, heads, num_workers) bytes (the kernels read their
- *             own records at offsets given by these arguments; a plan whose header names other
- *             arguments is reported, as below, and writes no output).
+ * plan        device plan from mla_get_split_plan for the same arguments.
  * num_workers the num_workers given to mla_get_split_plan.
  * workspace   device buffer of at least mla_workspace_bytes(batch, s_q, heads,
  *             num_workers) bytes, 16-byte aligned, or NULL when that size is 0. Scratch:
@@ -257,8 +253,7 @@ int32_t mla_get_sparse_plan(const int32_t* indices, int32_t topk, const int32_t*
 
 /* q, out, lse as for mla_decode_fwd ([batch, s_q, 128, ...]). kv_cache, kv_scales: the fp8 cache
  * (kv_dtype must be MLA_KV_FP8_E4M3; a bf16 cache is MLA_ERR_UNSUPPORTED here). rows, plan: from
- * mla_get_sparse_plan with the same batch, s_q, heads, topk, num_pages and num_workers, in their
- * buffers of the sizes given there.
+ * mla_get_sparse_plan with the same batch, s_q, heads, topk, num_pages and num_workers.
  * workspace: >= mla_workspace_bytes(batch * s_q, 1, 128, num_workers) bytes (or NULL when that is
  * 0), 16-byte aligned. status: as for mla_decode_fwd. Results for a fixed plan are bitwise
  * reproducible.

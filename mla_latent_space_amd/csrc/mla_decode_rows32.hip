@@ -1126,17 +1126,19 @@ __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32
   __shared__ __attribute__((aligned(16))) float row_resc[32];
   __shared__ __attribute__((aligned(16))) float row_t[32];
   __shared__ float row_m[32];
-  // The header and this block's split record in one round trip: the record area holds n_items
-  // entries, so the read is in bounds for every block of the grid, and no record word is used
-  // unless the header matches the call's arguments.
-  const PlanHead ph = load_plan_head(plan, plan + plan_split_off(n_items, workers) + kSplitWords * blockIdx.x);
-  if (!plan_header_matches(ph.h, batch, s_q, heads, causal, workers, n_items)) {
+  // The header (one 16-word load) is checked before this block's split record is read: a plan
+  // built for other arguments may sit in a smaller buffer, so no offset derived from the call's
+  // arguments is read until the header matches them. (The record area holds n_items entries,
+  // so the read is then in bounds for every block of the grid.)
+  const i32x16 hd = load_plan_header(plan);
+  if (!plan_header_matches(hd, batch, s_q, heads, causal, workers, n_items)) {
     if (status != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
       __hip_atomic_fetch_or(status, (int)kDevPlanMismatch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  if ((int)blockIdx.x >= ph.h[kHSplitItems]) return;
-  const int seq = ph.rec[kSSeq], tile = ph.rec[kSTile], ns_all = ph.rec[kSNsplits], slot0 = ph.rec[kSSlot];
+  if ((int)blockIdx.x >= hd[kHSplitItems]) return;
+  const int32_t* sr = plan + plan_split_off(n_items, workers) + kSplitWords * blockIdx.x;
+  const int seq = sr[kSSeq], tile = sr[kSTile], ns_all = sr[kSNsplits], slot0 = sr[kSSlot];
   const int rows_total = s_q * heads;
   const int rows_item = rows_total - kRowsPerTile * tile < kRowsPerTile ? rows_total - kRowsPerTile * tile
                                                                          : kRowsPerTile;

@@ -208,20 +208,10 @@ __device__ __forceinline__ int xcd_worker() {
 
 typedef __attribute__((ext_vector_type(16))) int i32x16;
 
-// The plan header (16 words) and one 4-word record of the plan, read in one round trip: both
-// are loaded whole and waited for together before anything looks at them (written as a chain
-// of ||, the header check compiles to one scalar load, compare and branch per word). The
-// record's words are only meaningful once the header matches the call's arguments.
-struct PlanHead {
-  i32x16 h;
-  i32x4 rec;
-};
-__device__ __forceinline__ PlanHead load_plan_head(const int32_t* __restrict__ plan, const int32_t* __restrict__ rec) {
-  PlanHead p;
-  p.h = *reinterpret_cast<const i32x16*>(plan);
-  p.rec = *reinterpret_cast<const i32x4*>(rec);
-  asm volatile("" : : "s"(p.h), "s"(p.rec));
-  return p;
+// The plan header (16 words) in one scalar load: written as a chain of ||, the header check
+// compiles to one scalar load, compare and branch per word.
+__device__ __forceinline__ i32x16 load_plan_header(const int32_t* __restrict__ plan) {
+  return *reinterpret_cast<const i32x16*>(plan);
 }
 // The header's identity words against the call's arguments.
 __device__ __forceinline__ bool plan_header_matches(const i32x16& h, int batch, int s_q, int heads, int causal,
