@@ -1097,22 +1097,14 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
 // O_k (unnormalised, relative to its reference max m_k, log2 units) and its denominator l_k:
 // with M = max_k m_k and a_k = 2^(m_k - M), out = sum_k a_k O_k / sum_k a_k l_k and
 // lse = (M + log2 sum_k a_k l_k) ln 2 (parts with no visible key have m_k = -inf, weight 0).
-// Fragment (w, c, lane) of a part is 32 contiguous bytes: 16 bf16, value r at row
-// 32w + 8(r/4) + 4(lane/32) + r%4 and channel 32c + lane%32, so a 32-row group of a
-// 128-channel quarter is 8 contiguous KiB per part. One block per (split item, group g,
-// quarter cq) takes the item's 32-row groups w = g, g + kCmbGroups, ...; the merged rows leave
-// through LDS as 512-B row segments. Items of at most kCmbBatch parts (the common case) request
-// the next group's data and (m, l) before the current group is merged and written, so that
-// one group's loads overlap the other's stores: every block starts at once, and with one group
-// per block all of the chip's reads would come before all of its writes.
-template <int N>
-struct IntC {
-  static constexpr int value = N;
-};
+// One block per (split item, 32-row group w, 128-channel quarter cq). Fragment (w, c, lane)
+// of a part is 32 contiguous bytes: 16 bf16, value r at row 32w + 8(r/4) + 4(lane/32) + r%4
+// and channel 32c + lane%32, so a block reads 8 contiguous KiB per part. The data loads of
+// the first parts are issued before the weights are formed; the merged rows leave through
+// LDS as 512-B row segments.
 constexpr int kCmbThreads = 256;
 constexpr int kCmbMaxSplits = 64;    // parts merged per pass over the weights (LDS: 2 x 8 KiB)
 constexpr int kCmbBatch = 4;         // parts whose data is in flight together
-constexpr int kCmbGroups = 2;        // blocks per (split item, channel quarter)
 
 __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32_t* __restrict__ plan,
                                                                      const char* __restrict__ ws,
@@ -1140,17 +1132,89 @@ __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32
   const int32_t* sr = plan + plan_split_off(n_items, workers) + kSplitWords * blockIdx.x;
   const int seq = sr[kSSeq], tile = sr[kSTile], ns_all = sr[kSNsplits], slot0 = sr[kSSlot];
   const int rows_total = s_q * heads;
-  const int rows_item = rows_total - kRowsPerTile * tile < kRowsPerTile ? rows_total - kRowsPerTile * tile
-                                                                         : kRowsPerTile;
-  const int nw = (rows_item + 31) / 32;   // 32-row groups that hold rows
-  const int g = blockIdx.y, cq = blockIdx.z;
+  const int w = blockIdx.y, cq = blockIdx.z;
+  if (kRowsPerTile * tile + 32 * w >= rows_total) return;
   const int tid = threadIdx.x;
   const int c = 4 * cq + (tid >> 6), ln = tid & 63, h = ln >> 5;
-  auto frag_of = [&](int w) -> int64_t { return 32 * (int64_t)((w * 16 + c) * 64 + ln); };
-  // Group w's merged rows out: acc holds this thread's 16 values (rows 8j + 4h + e of the group,
-  // channel 32c + ln%32), row_t and row_m the rows' sums and maxima. Ends with the block's LDS
-  // free for the next group.
-  auto emit = [&](int w, const float (&acc)[16]) {
+  const int64_t frag = 32 * (int64_t)((w * 16 + c) * 64 + ln);
+  // this thread's rows: 8j + 4h + v for register r = 4j + v
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  float m_old = -INFINITY, t_old = 0.f;   // per row, kept by threads tid < 32
+  for (int s0 = 0; s0 < ns_all; s0 += kCmbMaxSplits) {
+    const int ns = ns_all - s0 < kCmbMaxSplits ? ns_all - s0 : kCmbMaxSplits;
+    // data of the first parts in flight while the weights are formed
+    bf16x8 v[kCmbBatch][2];
+#pragma unroll
+    for (int b = 0; b < kCmbBatch; ++b)
+      if (b < ns) {
+        const char* p = ws + (int64_t)(slot0 + s0 + b) * kSlotBytes + frag;
+        v[b][0] = *reinterpret_cast<const bf16x8*>(p);
+        v[b][1] = *reinterpret_cast<const bf16x8*>(p + 16);
+      }
+    __syncthreads();
+    for (int idx = tid; idx < 32 * ns; idx += kCmbThreads) {
+      const int rr = idx & 31, sp = idx >> 5;
+      const float* stat = reinterpret_cast<const float*>(ws + (int64_t)(slot0 + s0 + sp) * kSlotBytes + kSlotPartBytes);
+      wts[sp][rr] = stat[32 * w + rr];
+      dens[sp][rr] = stat[kRowsPerTile + 32 * w + rr];
+    }
+    __syncthreads();
+    if (tid < 32) {
+      float m = m_old;
+      for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, wts[sp][tid]);
+      const float safe = m == -INFINITY ? 0.f : m;
+      const float resc = m_old == -INFINITY ? 0.f : exp2f(m_old - safe);
+      float tot = t_old * resc;
+      for (int sp = 0; sp < ns; ++sp) {
+        const float mk = wts[sp][tid];
+        const float wgt = mk == -INFINITY ? 0.f : exp2f(mk - safe);
+        wts[sp][tid] = wgt;
+        tot += wgt * dens[sp][tid];
+      }
+      m_old = m;
+      t_old = tot;
+      row_resc[tid] = resc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 rs4 = *reinterpret_cast<const f32x4*>(&row_resc[8 * j + 4 * h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * j + e] *= rs4[e];
+    }
+    for (int b0 = 0; b0 < ns; b0 += kCmbBatch) {
+      if (b0 > 0) {
+#pragma unroll
+        for (int b = 0; b < kCmbBatch; ++b)
+          if (b0 + b < ns) {
+            const char* p = ws + (int64_t)(slot0 + s0 + b0 + b) * kSlotBytes + frag;
+            v[b][0] = *reinterpret_cast<const bf16x8*>(p);
+            v[b][1] = *reinterpret_cast<const bf16x8*>(p + 16);
+          }
+      }
+#pragma unroll
+      for (int b = 0; b < kCmbBatch; ++b)
+        if (b0 + b < ns) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&wts[b0 + b][8 * j + 4 * h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * j + e;
+              acc[r] += w4[e] * (float)v[b][r >> 3][r & 7];
+            }
+          }
+        }
+    }
+  }
+  if (tid < 32) {
+    row_t[tid] = t_old;
+    row_m[tid] = m_old;
+  }
+  __syncthreads();
+  {
     const int cl = 32 * (c - 4 * cq) + (ln & 31);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1161,187 +1225,22 @@ __global__ __launch_bounds__(kCmbThreads) void combine_rows32_kernel(const int32
         tile_out[8 * j + 4 * h + e][cl] = acc[4 * j + e] * (t > 0.f ? 1.f / t : 0.f);
       }
     }
-    barrier_lds();
-    // 32 rows x 128 channels: 32 float4 per row
+  }
+  __syncthreads();
+  // 32 rows x 128 channels: 32 float4 per row
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + kCmbThreads * j;
-      const int rr = idx >> 5, c4 = (idx & 31) * 4;
-      const int grow = kRowsPerTile * tile + 32 * w + rr;
-      if (grow >= rows_total) continue;
-      const int jt = grow / heads, hd = grow - jt * heads;
-      const int64_t orow = (int64_t)(seq * s_q + jt) * heads + hd;
-      *reinterpret_cast<f32x4*>(out + orow * kLat + 128 * cq + c4) = *reinterpret_cast<const f32x4*>(&tile_out[rr][c4]);
-      if (cq == 0 && c4 == 0) {
-        const float t = row_t[rr];
-        lse[orow] = t > 0.f ? (row_m[rr] + __log2f(t)) * 0.6931471805599453f : -INFINITY;
-      }
+  for (int j = 0; j < 4; ++j) {
+    const int idx = tid + kCmbThreads * j;
+    const int rr = idx >> 5, c4 = (idx & 31) * 4;
+    const int grow = kRowsPerTile * tile + 32 * w + rr;
+    if (grow >= rows_total) continue;
+    const int jt = grow / heads, hd = grow - jt * heads;
+    const int64_t orow = (int64_t)(seq * s_q + jt) * heads + hd;
+    *reinterpret_cast<f32x4*>(out + orow * kLat + 128 * cq + c4) = *reinterpret_cast<const f32x4*>(&tile_out[rr][c4]);
+    if (cq == 0 && c4 == 0) {
+      const float t = row_t[rr];
+      lse[orow] = t > 0.f ? (row_m[rr] + __log2f(t)) * 0.6931471805599453f : -INFINITY;
     }
-    barrier_lds();
-  };
-
-  // Items of NS <= kCmbBatch parts. Every load here is unconditional, so that the compiler's
-  // vmcnt waits count exactly and none of them drains the next group's loads.
-  auto merge_few = [&](auto ns_c) {
-    constexpr int NS = decltype(ns_c)::value;
-    bf16x8 dv[2][NS][2];          // two groups' data
-    float st_m[2], st_l[2];       // two groups' (m, l) of row tid % 32, part tid / 32
-    // (threads past the NS parts read the last part's words and park them in rows NS..7 of
-    // the weight arrays, which the merge does not read: an unconditional use keeps the
-    // compiler from moving these loads behind a branch)
-    const int sr_row = tid & 31, sr_slot = tid >> 5, sr_part = sr_slot < NS ? sr_slot : NS - 1;
-    const float* stat = reinterpret_cast<const float*>(ws + (int64_t)(slot0 + sr_part) * kSlotBytes + kSlotPartBytes);
-    auto fetch = [&](int w, int buf) {
-      const int64_t frag = frag_of(w);
-#pragma unroll
-      for (int b = 0; b < NS; ++b) {
-        const char* p = ws + (int64_t)(slot0 + b) * kSlotBytes + frag;
-        dv[buf][b][0] = *reinterpret_cast<const bf16x8*>(p);
-        dv[buf][b][1] = *reinterpret_cast<const bf16x8*>(p + 16);
-      }
-      st_m[buf] = stat[32 * w + sr_row];
-      st_l[buf] = stat[kRowsPerTile + 32 * w + sr_row];
-    };
-    // group w from buffer buf: weights, then the weighted sum, then the rows out
-    auto merge = [&](int w, int buf) {
-      wts[sr_slot][sr_row] = st_m[buf];
-      dens[sr_slot][sr_row] = st_l[buf];
-      barrier_lds();
-      if (tid < 32) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int sp = 0; sp < NS; ++sp) m = fmaxf(m, wts[sp][tid]);
-        const float safe = m == -INFINITY ? 0.f : m;
-        float tot = 0.f;
-#pragma unroll
-        for (int sp = 0; sp < NS; ++sp) {
-          const float mk = wts[sp][tid];
-          const float wgt = mk == -INFINITY ? 0.f : exp2f(mk - safe);
-          wts[sp][tid] = wgt;
-          tot += wgt * dens[sp][tid];
-        }
-        row_t[tid] = tot;
-        row_m[tid] = m;
-      }
-      barrier_lds();
-      float acc[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-      for (int b = 0; b < NS; ++b) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 w4 = *reinterpret_cast<const f32x4*>(&wts[b][8 * j + 4 * h]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * j + e;
-            acc[r] += w4[e] * (float)dv[buf][b][r >> 3][r & 7];
-          }
-        }
-      }
-      emit(w, acc);
-    };
-    // Two straight-line paths (one group, or two with the second's loads issued first), so that
-    // no branch sits between a load and its wait.
-    static_assert(4 / kCmbGroups == 2, "a block takes at most two 32-row groups");
-    if (g + kCmbGroups < nw) {
-      fetch(g, 0);
-      fetch(g + kCmbGroups, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      merge(g, 0);
-      merge(g + kCmbGroups, 1);
-    } else {
-      fetch(g, 0);
-      merge(g, 0);
-    }
-  };
-  static_assert(kCmbBatch == 4, "merge_few instances");
-  if (g >= nw) return;
-  if (ns_all == 2) return merge_few(IntC<2>{});
-  if (ns_all == 3) return merge_few(IntC<3>{});
-  if (ns_all == 4) return merge_few(IntC<4>{});
-
-  // more parts: passes of up to kCmbMaxSplits weights, each over batches of kCmbBatch parts
-  for (int w = g; w < nw; w += kCmbGroups) {
-    const int64_t frag = frag_of(w);
-    float acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    float m_old = -INFINITY, t_old = 0.f;   // per row, kept by threads tid < 32
-    for (int s0 = 0; s0 < ns_all; s0 += kCmbMaxSplits) {
-      const int ns = ns_all - s0 < kCmbMaxSplits ? ns_all - s0 : kCmbMaxSplits;
-      // data of the first parts in flight while the weights are formed
-      bf16x8 v[kCmbBatch][2];
-#pragma unroll
-      for (int b = 0; b < kCmbBatch; ++b)
-        if (b < ns) {
-          const char* p = ws + (int64_t)(slot0 + s0 + b) * kSlotBytes + frag;
-          v[b][0] = *reinterpret_cast<const bf16x8*>(p);
-          v[b][1] = *reinterpret_cast<const bf16x8*>(p + 16);
-        }
-      for (int idx = tid; idx < 32 * ns; idx += kCmbThreads) {
-        const int rr = idx & 31, sp = idx >> 5;
-        const float* stat =
-            reinterpret_cast<const float*>(ws + (int64_t)(slot0 + s0 + sp) * kSlotBytes + kSlotPartBytes);
-        wts[sp][rr] = stat[32 * w + rr];
-        dens[sp][rr] = stat[kRowsPerTile + 32 * w + rr];
-      }
-      barrier_lds();
-      if (tid < 32) {
-        float m = m_old;
-        for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, wts[sp][tid]);
-        const float safe = m == -INFINITY ? 0.f : m;
-        const float resc = m_old == -INFINITY ? 0.f : exp2f(m_old - safe);
-        float tot = t_old * resc;
-        for (int sp = 0; sp < ns; ++sp) {
-          const float mk = wts[sp][tid];
-          const float wgt = mk == -INFINITY ? 0.f : exp2f(mk - safe);
-          wts[sp][tid] = wgt;
-          tot += wgt * dens[sp][tid];
-        }
-        m_old = m;
-        t_old = tot;
-        row_resc[tid] = resc;
-      }
-      barrier_lds();
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 rs4 = *reinterpret_cast<const f32x4*>(&row_resc[8 * j + 4 * h]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * j + e] *= rs4[e];
-      }
-      for (int b0 = 0; b0 < ns; b0 += kCmbBatch) {
-        if (b0 > 0) {
-#pragma unroll
-          for (int b = 0; b < kCmbBatch; ++b)
-            if (b0 + b < ns) {
-              const char* p = ws + (int64_t)(slot0 + s0 + b0 + b) * kSlotBytes + frag;
-              v[b][0] = *reinterpret_cast<const bf16x8*>(p);
-              v[b][1] = *reinterpret_cast<const bf16x8*>(p + 16);
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < kCmbBatch; ++b)
-          if (b0 + b < ns) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const f32x4 w4 = *reinterpret_cast<const f32x4*>(&wts[b0 + b][8 * j + 4 * h]);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 4 * j + e;
-                acc[r] += w4[e] * (float)v[b][r >> 3][r & 7];
-              }
-            }
-          }
-      }
-      barrier_lds();   // (the weights are rewritten by the next pass)
-    }
-    if (tid < 32) {
-      row_t[tid] = t_old;
-      row_m[tid] = m_old;
-    }
-    barrier_lds();
-    emit(w, acc);
   }
 }
 
@@ -1377,7 +1276,7 @@ hipError_t launch_decode_sparse_fp8(const DecodeArgs& a, const int32_t* rows, in
 hipError_t launch_combine_rows32(const DecodeArgs& a, hipStream_t stream) {
   const int n_items = a.batch * tiles_per_seq(a.s_q, a.heads);
   const int max_split = a.workers < n_items ? a.workers : n_items;   // split items <= both
-  hipLaunchKernelGGL(combine_rows32_kernel, dim3(max_split, kCmbGroups, 4), dim3(kCmbThreads), 0, stream,
+  hipLaunchKernelGGL(combine_rows32_kernel, dim3(max_split, kRowsPerTile / 32, 4), dim3(kCmbThreads), 0, stream,
                      a.plan, reinterpret_cast<const char*>(a.ws), a.out, a.lse, a.batch, a.s_q, a.heads, a.causal,
                      n_items, a.workers, a.status);
   return hipGetLastError();
