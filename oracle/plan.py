@@ -4,7 +4,7 @@ The FlashMLA-2 newsletter page (section "Architectural Analysis") describes a
 radix-sorted block scheduler that balances the partitions of the sequences of one
 batch across compute units, so that a 128-token sequence and a 128k-token sequence in
 the same batch do not leave stragglers. The pages give no more detail; the plan below
-is this build's plain reading of that sentence, written out as a definition so that
+is the plainest reading of that description, written out as a definition so that
 the device planner can be checked against it bit for bit:
 
 1. Work items. Each sequence i contributes ceil(s_q * h / 128) row tiles of 128
