@@ -66,6 +66,18 @@ __global__ __launch_bounds__(kHyThreads, 2) void hybrid_new_kernel(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qb[8 + ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
   }
+  // The old part's (out, lse) of the rows this thread merges at the end (row tid / 8, channels
+  // 32k + 4 (tid % 8) .. +3), requested now so that their latency passes during the new tokens
+  // instead of after them.
+  const int m_rr = threadIdx.x >> 3, m_q4 = 4 * (threadIdx.x & 7);
+  f32x4 ov_pre[4];
+  float lo_pre = -INFINITY;
+  if (m_rr < S) {
+    const int64_t orow = ((int64_t)b * S + m_rr) * H + h;
+    lo_pre = lse_old[orow];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ov_pre[k] = *reinterpret_cast<const f32x4*>(out_old + orow * 128 + 32 * k + m_q4);
+  }
   // new tokens visible to this lane's row (0 for padding rows)
   const int lim = row < S ? (causal ? N - S + 1 + row : N) : 0;
 
@@ -211,10 +223,10 @@ __global__ __launch_bounds__(kHyThreads, 2) void hybrid_new_kernel(
   __syncthreads();
   {
     // thread: row tid / 8, channels 32k + 4(tid % 8) .. +3 for k = 0..3
-    const int tid = threadIdx.x, rr = tid >> 3, q4 = 4 * (tid & 7);
+    const int tid = threadIdx.x, rr = m_rr, q4 = m_q4;
     if (rr < S) {
       const int64_t orow = ((int64_t)b * S + rr) * H + h;
-      const float lo = lse_old[orow];
+      const float lo = lo_pre;
       const float m_old = lo == -INFINITY ? -INFINITY : lo * 1.4426950408889634f;
       float M = m_old;
 #pragma unroll
@@ -234,7 +246,7 @@ __global__ __launch_bounds__(kHyThreads, 2) void hybrid_new_kernel(
         const int c0 = 32 * k + q4;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (a_old != 0.f) {
-          const f32x4 ov = *reinterpret_cast<const f32x4*>(out_old + orow * 128 + c0);
+          const f32x4 ov = ov_pre[k];
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[e] = a_old * ov[e];
         }
