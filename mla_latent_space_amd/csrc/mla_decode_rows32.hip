@@ -914,23 +914,23 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
         //    k-step 0 for the other row blocks, then k-step 1 channel tile by channel tile
         {
           const PvAddr pa = pv_at(pv0, zc);
-          bf16x8 bq1[3];   // ring of Z^T tiles of k-step 1
+          bf16x8 bq1[4];   // Z^T tiles of k-step 1
           bf16x8 aq1[3];   // P tiles of k-step 1, the other row blocks
 #pragma unroll
           for (int t = kR32PvLead; t < 32; ++t) {
-            if (t == 6) bq1[0] = pv_read(pa, 16 + 0);
+            if (t == 5) bq1[0] = pv_read(pa, 16 + 0);
             if (t == 8) aq1[0] = a_read(1, 1);
             if (t == 9) aq1[1] = a_read(2, 1);
             if (t == 10) aq1[2] = a_read(3, 1);
-            if (t == 12) bq1[1] = pv_read(pa, 16 + 1);
-            if (t == 16) bq1[2] = pv_read(pa, 16 + 2);
-            if (t == 20) bq1[0] = pv_read(pa, 16 + 3);
+            if (t == 7) bq1[1] = pv_read(pa, 16 + 1);
+            if (t == 11) bq1[2] = pv_read(pa, 16 + 2);
+            if (t == 13) bq1[3] = pv_read(pa, 16 + 3);
             if (t < 16) {
               const int g = 1 + (t - 4) / 4, c = (t - 4) % 4;
               mfma_a(o[4 * g + c], aq0[g - 1], bq0[c]);
             } else {
               const int c = (t - 16) / 4, g = (t - 16) % 4;
-              mfma_a(o[4 * g + c], g == 0 ? pcur[1] : aq1[g == 0 ? 0 : g - 1], bq1[c % 3]);
+              mfma_a(o[4 * g + c], g == 0 ? pcur[1] : aq1[g == 0 ? 0 : g - 1], bq1[c]);
             }
             // one softmax piece after each value MFMA
             const int u = t - kR32PvLead;
