@@ -45,6 +45,8 @@ def _new_tokens(b, n, h, gen):
     (16, 16, 33, True, [64, 100, 1]),
     (32, 16, 200, False, [0, 0, 0]),
     (2, 64, 200, True, [300, 33, 0]),
+    (32, 16, 64, True, [10, 0, 500]),        # the largest query tile, causal
+    (16, 128, 640, True, [300]),             # the benchmark's s_q, heads and new tokens (one sequence)
 ])
 def test_merge_matches_oracle(s_q, heads, n, causal, o_lens):
     b = len(o_lens)
