@@ -261,15 +261,12 @@ __global__ __launch_bounds__(kR32Threads, 1) void decode_rows32_kernel(
     if (status != nullptr && dev_err != 0 && threadIdx.x == 0)
       __hip_atomic_fetch_or(status, dev_err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  if (plan[kHMagic] != kPlanMagic || plan[kHVersion] != kPlanVersion || plan[kHWorkers] != (int)gridDim.x ||
-      plan[kHBatch] != a.batch ||
-      plan[kHSq] != a.s_q || plan[kHHeads] != a.heads || plan[kHCausal] != a.causal ||
-      plan[kHItems] != a.batch * tiles_per_seq(a.s_q, a.heads)) {
+  const int n_items = a.batch * tiles_per_seq(a.s_q, a.heads);
+  if (!plan_header_matches(load_plan_header(plan), a.batch, a.s_q, a.heads, a.causal, (int)gridDim.x, n_items)) {
     dev_err = kDevPlanMismatch;
     report();
     return;
   }
-  const int n_items = plan[kHItems];
   const int32_t* wr = plan + plan_workers_off(n_items) + kWorkerWords * worker;
   const int kb = wr[0], pb = wr[1], ke = wr[2], pe = wr[3];
   int k_last = pe > 0 ? ke : ke - 1;
