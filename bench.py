@@ -382,6 +382,8 @@ def main():
                     help="also time the split latent + decompressed variant (its latent part runs the same decode "
                          "kernel, so it stays out of the default run's kernel trace)")
     ap.add_argument("--sparse", action="store_true", help="also time the token-sparse fp8 decode")
+    ap.add_argument("--no-measured", action="store_true",
+                    help="skip the microbenchmarks that measure this device's stream-read rate and MFMA peak")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times (the reference "
                          "kernel for scaling HBM byte counters), print its size and exit")
@@ -503,6 +505,14 @@ def main():
         "roofline": dict(roof, kernel="mla_decode_fwd: decode_rows32_kernel, then combine_rows32_kernel (the "
                                       "merge of split items)", bytes_per_call=byts, flops_per_call=flops),
     }
+    if not args.no_measured:
+        # after the timed steps: the same fractions against what this device reaches with a plain
+        # read stream and with MFMA chains alone (the headline keeps the published peaks)
+        from mla_latent_space_amd import roofbench
+        m = roofbench.measure(0)
+        m["decode_frac_of_stream_read"] = round(achieved_gbps / m["stream_read_gbps"], 4)
+        m["decode_frac_of_mfma_loop"] = round(tflops / m["mfma_bf16_tflops"]["1_wave_per_simd"], 4)
+        rec["measured_denominators"] = m
     if w.kv_dtype == "bf16" and not args.no_projections:
         rec["projections"] = projections(w, args.steps, min(args.warmup, 50))
     if args.hybrid:
