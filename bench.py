@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "MLA decode µs/call, TFLOPS + HBM GB/s (% roofline), b=64 h=128 t=4096 bf16"
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 K_LAT, P_ROPE = 512, 64
 
 
@@ -451,20 +452,27 @@ def main():
     stream = torch.cuda.current_stream()
     # (at least 200 calls each, so that a short run still averages over a steady state)
     plan = mla.get_split_plan(sl, w.s_q, w.heads, w.causal, W, out=plan_buf)
-    n_calls = max(args.steps, 200)
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    # events after every chunk of 10 calls as well (a marker on the stream, no gap between
+    # calls): the chunk means give the spread
+    chunk = 10
+    n_calls = max(args.steps, 200) // chunk * chunk
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_calls // chunk + 1)]
+    e2 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    e0.record(stream)
+    ev[0].record(stream)
     for i in range(n_calls):
         mla.decode_fwd(q, kvs[i % rot], bt, sl, w.scale, kv_scales=scs[i % rot], causal=w.causal, plan=plan,
                        workspace=ws, out=out, lse=lse)
-    e1.record(stream)
+        if (i + 1) % chunk == 0:
+            ev[(i + 1) // chunk].record(stream)
     for i in range(n_calls):
         mla.get_split_plan(sl, w.s_q, w.heads, w.causal, W, out=plan_buf)
     e2.record(stream)
     torch.cuda.synchronize()
-    dec_mean = e0.elapsed_time(e1) * 1e3 / n_calls
-    plan_mean = e1.elapsed_time(e2) * 1e3 / n_calls
+    dec_mean = ev[0].elapsed_time(ev[-1]) * 1e3 / n_calls
+    plan_mean = ev[-1].elapsed_time(e2) * 1e3 / n_calls
+    chunk_us = np.array([ev[c].elapsed_time(ev[c + 1]) * 1e3 / chunk for c in range(len(ev) - 1)])
+    dec_pct = [round(float(np.percentile(chunk_us, p)), 2) for p in (10, 50, 90)]
 
     flops = workload_flops(w)
     byts = workload_bytes(w)
@@ -496,6 +504,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(w), "kv_copies_rotated": rot, "num_workers": W},
         "decode_us": round(dec_mean, 2),
+        "decode_us_p10_p50_p90": dec_pct,
         "plan_us": round(plan_mean, 2),
         "tflops": round(tflops, 1),
         "hbm_gbps": round(achieved_gbps, 1),
@@ -505,6 +514,13 @@ def main():
         "roofline": dict(roof, kernel="mla_decode_fwd: decode_rows32_kernel, then combine_rows32_kernel (the "
                                       "merge of split items)", bytes_per_call=byts, flops_per_call=flops),
     }
+    if w.kv_dtype == "fp8":
+        # the same call priced as if its products ran in fp8 (the kernel dequantises to bf16 and
+        # runs bf16 MFMAs): then the HBM time of its 656-B rows bounds it
+        hbm_us, f8_us = byts / (PEAK_HBM_GBPS * 1e9) * 1e6, flops / (PEAK_FP8_TFLOPS * 1e12) * 1e6
+        rec["bound_with_fp8_math"] = {"bound": "hbm" if hbm_us >= f8_us else "mfma",
+                                      "bound_us": round(max(hbm_us, f8_us), 2),
+                                      "frac": round(max(hbm_us, f8_us) / dec_mean, 4)}
     if not args.no_measured:
         # after the timed steps: the same fractions against what this device reaches with a plain
         # read stream and with MFMA chains alone (the headline keeps the published peaks)
