@@ -410,6 +410,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": nbytes, "calls": args.steps}), flush=True)
         return
     w = wl.make_config(args.workload)
+    print(f"[bench] {args.workload} inputs drawn", file=sys.stderr, flush=True)
     dev = torch.device("cuda", 0)
     q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
     if w.kv_dtype == "bf16":
@@ -536,6 +537,7 @@ def main():
     if args.sparse:
         rec["sparse"] = sparse(min(args.steps, 100), min(args.warmup, 50))
     if not args.no_cpu:
+        print("[bench] GPU legs done; timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
