@@ -27,6 +27,7 @@ namespace {
 constexpr int kProjThreads = 256;
 constexpr int kProjKc = 128;                  // k per chunk
 constexpr int kProjBBytes = 128 * kProjKc * 2;   // B block: 128 rows x 128 k, bf16 (32 KiB)
+constexpr int kProjSmallTokens = 64;             // up to this many tokens: 32-token tiles
 
 // LDS-DMA of a block of `rows` rows x kProjKc elements of `esz` bytes from a row-major source
 // (row stride `src_stride` bytes, block start at byte `src0` of the buffer): LDS holds row r at
@@ -45,19 +46,29 @@ __device__ __forceinline__ void stage_block(const i32x4& rsrc, uint32_t lds_dst,
   }
 }
 
-// DMA instructions one wave issues for one chunk (B block, then A block)
-template <bool kAFloat>
+// DMA instructions one wave issues for one chunk (B block, then A block of kMT rows)
+template <bool kAFloat, int kMT>
 constexpr int chunk_dma_per_wave() {
-  return (128 * kProjKc * 2 / 16 / 64 + 32 * kProjKc * (kAFloat ? 4 : 2) / 16 / 64) / 4;
+  return (128 * kProjKc * 2 / 16 / 64 + kMT * kProjKc * (kAFloat ? 4 : 2) / 16 / 64) / 4;
 }
 
 // C[t, h, n] = sum_k A[t, h, k] B[h, n, k] for n < N (A rows of K elements, C rows of ldc
 // elements); with a rope operand, C[t, h, N .. N+63] = rope[t, h, 0 .. 63] as well. kDb: two
-// LDS buffers (K > kProjKc).
-template <bool kAFloat, bool kCBf16, bool kDb>
+// LDS buffers (K > kProjKc). kMT: tokens per work-group (32, 64 or 128); each wave multiplies
+// its 32 columns of the weight block with every 32-row block of the token tile, so a weight
+// fragment read from LDS serves kMT / 32 MFMAs and the weight block is staged once per kMT
+// tokens.
+// bf16 output (the absorption): the MFMA takes the weight rows as its first operand, so a
+// lane's accumulator holds one token and runs of four consecutive columns; the tile goes to
+// LDS as 8-B runs (16-B chunks XOR-swizzled by row) and leaves as whole 256-B row segments,
+// 16 B per thread. fp32 output (the decompression): a lane holds one column and 16 rows, so
+// each store instruction already writes two whole 128-B row segments.
+template <bool kAFloat, bool kCBf16, bool kDb, int kMT>
 __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restrict__ A, const __bf16* __restrict__ B,
                                                             void* __restrict__ C, const __bf16* __restrict__ rope,
                                                             int T, int H, int K, int N, int ldc) {
+  static_assert(kMT == 32 || kMT == 64 || kMT == 128, "token tile");
+  constexpr int kRB = kMT / 32;   // 32-row blocks per tile
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   char __attribute__((address_space(3)))* lds = (char __attribute__((address_space(3)))*)smem_raw;
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
@@ -66,25 +77,27 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // block -> (column tile, token tile, head): the token tiles of one (head, column tile), which read
   // the same weight block, share a block-index residue mod 8 and so an XCD and its L2
-  const int ncol = N / 128, ntile = (T + 31) / 32;
+  const int ncol = N / 128, ntile = (T + kMT - 1) / kMT;
   const int lin = blockIdx.x, x8 = lin & 7, r = lin >> 3;
   const int ytile = r % ntile, pair = (r / ntile) * 8 + x8;
   if (pair >= ncol * H) return;
-  const int h = pair / ncol, m0 = 32 * ytile, nb = 128 * (pair - h * ncol);
+  const int h = pair / ncol, m0 = kMT * ytile, nb = 128 * (pair - h * ncol);
   // A: all T rows of head h; row m at byte (m H + h) K esz; the range check zero-fills m >= T
   const i32x4 ra = make_rsrc(reinterpret_cast<uint64_t>(A), (int)((int64_t)T * H * K * esz));
   // B: rows nb .. nb+127 of head h, K elements each
   const i32x4 rb = make_rsrc(reinterpret_cast<uint64_t>(B) + ((uint64_t)h * N + nb) * K * 2, 128 * K * 2);
-  constexpr uint32_t kBufBytesP = kProjBBytes + 32 * a_row_bytes;   // one buffer: B block, then A block
-  f32x16 acc;
+  constexpr uint32_t kBufBytesP = kProjBBytes + kMT * a_row_bytes;   // one buffer: B block, then A block
+  f32x16 acc[kRB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int i = 0; i < kRB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   const int l32 = lane & 31, hh = lane >> 5;
   const int nrow = 32 * wave + l32;   // this lane's row of the B block
   auto stage = [&](int kc, uint32_t buf) {
     stage_block(rb, lds_u32 + buf, (uint32_t)kc * 2, (uint32_t)K * 2, 128, 2, tid);
     stage_block(ra, lds_u32 + buf + kProjBBytes, (uint32_t)(((int64_t)m0 * H + h) * K + kc) * esz,
-                (uint32_t)H * K * esz, 32, esz, tid);
+                (uint32_t)H * K * esz, kMT, esz, tid);
   };
   if (kDb) stage(0, 0u);
   for (int kc = 0; kc < K; kc += kProjKc) {
@@ -92,7 +105,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
     if (kDb) {
       if (kc + kProjKc < K) {
         stage(kc + kProjKc, kBufBytesP - buf);   // the next chunk into the other buffer
-        wait_vmcnt<chunk_dma_per_wave<kAFloat>()>();
+        wait_vmcnt<chunk_dma_per_wave<kAFloat, kMT>()>();
       } else {
         wait_vmcnt<0>();
       }
@@ -105,81 +118,137 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
     for (int j = 0; j < kProjKc / 16; ++j) {
       const int c = 2 * j + hh;   // logical 16-B chunk of k 16j + 8hh .. +7 (bf16)
       const bf16x8 bf = lds_b128(lds + (buf + nrow * 256 + 16 * (c ^ (nrow & 15))));
-      bf16x8 af;
-      if (kAFloat) {
-        // fp32: the 8 values are logical chunks 2c, 2c+1 of a 512-B row
-        const f32x4 lo = *(const f32x4 __attribute__((address_space(3)))*)(
-            lds + (buf + kProjBBytes + l32 * a_row_bytes + 16 * ((2 * c) ^ (l32 & 15))));
-        const f32x4 hi = *(const f32x4 __attribute__((address_space(3)))*)(
-            lds + (buf + kProjBBytes + l32 * a_row_bytes + 16 * ((2 * c + 1) ^ (l32 & 15))));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          af[i] = (__bf16)lo[i];
-          af[4 + i] = (__bf16)hi[i];
+      for (int i = 0; i < kRB; ++i) {
+        // A row 32 i + l32 of the tile (the swizzle depends on the row's low 4 bits only)
+        const uint32_t arow = buf + kProjBBytes + (uint32_t)(32 * i + l32) * a_row_bytes;
+        bf16x8 af;
+        if (kAFloat) {
+          // fp32: the 8 values are logical chunks 2c, 2c+1 of a 512-B row
+          const f32x4 lo = *(const f32x4 __attribute__((address_space(3)))*)(lds + (arow + 16 * ((2 * c) ^ (l32 & 15))));
+          const f32x4 hi =
+              *(const f32x4 __attribute__((address_space(3)))*)(lds + (arow + 16 * ((2 * c + 1) ^ (l32 & 15))));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            af[q] = (__bf16)lo[q];
+            af[4 + q] = (__bf16)hi[q];
+          }
+        } else {
+          af = lds_b128(lds + (arow + 16 * (c ^ (l32 & 15))));
         }
-      } else {
-        af = lds_b128(lds + (buf + kProjBBytes + l32 * a_row_bytes + 16 * (c ^ (l32 & 15))));
+        if (kCBf16) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc[i], 0, 0, 0);
+        else acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[i], 0, 0, 0);
       }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
     }
-    barrier_lds();   // the blocks are read before a later chunk overwrites them
+    barrier_lds();   // the blocks are read before a later chunk (or the output tile) overwrites them
   }
-  const int n0 = nb + 32 * wave;
-  // acc register r of lane l: row m0 + 8(r/4) + 4(l/32) + r%4, column n0 + l%32
+  if constexpr (kCBf16) {
+    // acc[i] register 4q + v of lane l: token 32 i + l%32 of the tile, column 32 wave + 8q + 4(l/32) + v
+    // -> LDS row t (256 B), 16-B chunk (4 wave + q) ^ (t % 16), bytes 8(l/32) .. +7
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = m0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-    if (m >= T) continue;
-    const int64_t ci = ((int64_t)m * H + h) * ldc + n0 + l32;
-    if (kCBf16) static_cast<__bf16*>(C)[ci] = (__bf16)acc[r];
-    else static_cast<float*>(C)[ci] = acc[r];
+    for (int i = 0; i < kRB; ++i) {
+      const uint32_t t = (uint32_t)(32 * i + l32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[i][4 * q + e];
+        const uint32_t off = t * 256u + 16u * (((uint32_t)(4 * wave + q)) ^ (t & 15u)) + 8u * (uint32_t)hh;
+        *(bf16x4 __attribute__((address_space(3)))*)(lds + off) = v;
+      }
+    }
+    barrier_lds();
+    // row t, logical chunk q (columns nb + 8q .. +7): 16 threads per row
+#pragma unroll
+    for (int s2 = 0; s2 < kMT * 16 / kProjThreads; ++s2) {
+      const int k = tid + kProjThreads * s2;
+      const int t = k >> 4, q = k & 15;
+      const int m = m0 + t;
+      const u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(lds + (t * 256 + 16 * (q ^ (t & 15))));
+      if (m < T) {
+        const int64_t ci = ((int64_t)m * H + h) * ldc + nb + 8 * q;
+        *reinterpret_cast<u32x4*>(static_cast<__bf16*>(C) + ci) = v;
+      }
+    }
+  } else {
+    const int n0 = nb + 32 * wave;
+    // acc[i] register r of lane l: row m0 + 32 i + 8(r/4) + 4(l/32) + r%4, column n0 + l%32
+#pragma unroll
+    for (int i = 0; i < kRB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (m >= T) continue;
+        static_cast<float*>(C)[((int64_t)m * H + h) * ldc + n0 + l32] = acc[i][r];
+      }
   }
   if (rope != nullptr && nb == 0) {
-    // 32 rows x 64 rope values (128 B per row): one 16-B chunk per thread
-    const int rr = tid >> 3, ch = tid & 7;
-    const int m = m0 + rr;
-    if (m < T) {
-      const int64_t src = ((int64_t)m * H + h) * 64 + 8 * ch;
-      const int64_t dst = ((int64_t)m * H + h) * ldc + N + 8 * ch;
-      *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(C) + dst) = *reinterpret_cast<const bf16x8*>(rope + src);
+    // kMT rows x 64 rope values (128 B per row): one 16-B chunk per thread and pass
+#pragma unroll
+    for (int s2 = 0; s2 < kMT * 8 / kProjThreads; ++s2) {
+      const int k = tid + kProjThreads * s2;
+      const int rr = k >> 3, ch = k & 7;
+      const int m = m0 + rr;
+      if (m < T) {
+        const int64_t src = ((int64_t)m * H + h) * 64 + 8 * ch;
+        const int64_t dst = ((int64_t)m * H + h) * ldc + N + 8 * ch;
+        *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(C) + dst) = *reinterpret_cast<const bf16x8*>(rope + src);
+      }
     }
   }
 }
 
-constexpr int proj_lds_bytes(bool a_float, bool db) {
-  return (db ? 2 : 1) * (kProjBBytes + 32 * kProjKc * (a_float ? 4 : 2));
+constexpr int proj_lds_bytes(bool a_float, bool db, int mt) {
+  return (db ? 2 : 1) * (kProjBBytes + mt * kProjKc * (a_float ? 4 : 2));
+}
+
+// token tiles: 32 for a few tokens (more work-groups), larger ones when the weight block would
+// otherwise be staged again for every 32 tokens
+template <int kMT>
+void absorb_launch(const void* q_nope, const void* q_rope, const void* w_k, int tokens, int heads, void* qz,
+                   hipStream_t stream) {
+  const int pairs = (kLat / 128) * heads;
+  const dim3 grid(((pairs + 7) / 8) * 8 * ((tokens + kMT - 1) / kMT));
+  hipLaunchKernelGGL((proj_kernel<false, true, false, kMT>), grid, dim3(kProjThreads), proj_lds_bytes(false, false, kMT),
+                     stream, q_nope, static_cast<const __bf16*>(w_k), qz, static_cast<const __bf16*>(q_rope), tokens,
+                     heads, kNope, kLat, kDqk);
+}
+
+template <int kMT>
+hipError_t decompress_launch(const float* out_latent, const void* w_v, int tokens, int heads, float* out,
+                             hipStream_t stream) {
+  static thread_local int configured = -1;   // the LDS opt-in (two buffers) is per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (configured != dev) {
+    e = hipFuncSetAttribute((const void*)proj_kernel<true, false, true, kMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            proj_lds_bytes(true, true, kMT));
+    if (e != hipSuccess) return e;
+    configured = dev;
+  }
+  const int pairs = heads;
+  const dim3 grid(((pairs + 7) / 8) * 8 * ((tokens + kMT - 1) / kMT));
+  hipLaunchKernelGGL((proj_kernel<true, false, true, kMT>), grid, dim3(kProjThreads), proj_lds_bytes(true, true, kMT),
+                     stream, static_cast<const void*>(out_latent), static_cast<const __bf16*>(w_v),
+                     static_cast<void*>(out), static_cast<const __bf16*>(nullptr), tokens, heads, kLat, kDv, kDv);
+  return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int tokens, int heads,
                                void* qz, hipStream_t stream) {
-  const int pairs = (kLat / 128) * heads;
-  const dim3 grid(((pairs + 7) / 8) * 8 * ((tokens + 31) / 32));
-  hipLaunchKernelGGL((proj_kernel<false, true, false>), grid, dim3(kProjThreads), proj_lds_bytes(false, false), stream,
-                     q_nope,
-                     static_cast<const __bf16*>(w_k), qz, static_cast<const __bf16*>(q_rope), tokens, heads,
-                     kNope, kLat, kDqk);
+  if (tokens <= kProjSmallTokens) absorb_launch<32>(q_nope, q_rope, w_k, tokens, heads, qz, stream);
+  else absorb_launch<128>(q_nope, q_rope, w_k, tokens, heads, qz, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_decompress_output(const float* out_latent, const void* w_v, int tokens, int heads, float* out,
                                     hipStream_t stream) {
-  static thread_local int configured = -1;   // the LDS opt-in (96 KiB, two buffers) is per device
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  const hipError_t e = tokens <= kProjSmallTokens ? decompress_launch<32>(out_latent, w_v, tokens, heads, out, stream)
+                                                   : decompress_launch<64>(out_latent, w_v, tokens, heads, out, stream);
   if (e != hipSuccess) return e;
-  if (configured != dev) {
-    e = hipFuncSetAttribute((const void*)proj_kernel<true, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            proj_lds_bytes(true, true));
-    if (e != hipSuccess) return e;
-    configured = dev;
-  }
-  const int pairs = heads;
-  const dim3 grid(((pairs + 7) / 8) * 8 * ((tokens + 31) / 32));
-  hipLaunchKernelGGL((proj_kernel<true, false, true>), grid, dim3(kProjThreads), proj_lds_bytes(true, true), stream,
-                     static_cast<const void*>(out_latent), static_cast<const __bf16*>(w_v), static_cast<void*>(out),
-                     static_cast<const __bf16*>(nullptr), tokens, heads, kLat, kDv, kDv);
   return hipGetLastError();
 }
 
