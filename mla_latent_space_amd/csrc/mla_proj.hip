@@ -68,6 +68,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
                                                             void* __restrict__ C, const __bf16* __restrict__ rope,
                                                             int T, int H, int K, int N, int ldc) {
   static_assert(kMT == 32 || kMT == 64 || kMT == 128, "token tile");
+  // (with a rope operand N = 512: four column tiles, kMT / 4 rope rows each, at most 256 threads' worth)
   constexpr int kRB = kMT / 32;   // 32-row blocks per tile
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   char __attribute__((address_space(3)))* lds = (char __attribute__((address_space(3)))*)smem_raw;
@@ -87,6 +88,21 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
   // B: rows nb .. nb+127 of head h, K elements each
   const i32x4 rb = make_rsrc(reinterpret_cast<uint64_t>(B) + ((uint64_t)h * N + nb) * K * 2, 128 * K * 2);
   constexpr uint32_t kBufBytesP = kProjBBytes + kMT * a_row_bytes;   // one buffer: B block, then A block
+  // rope rows of the tile (16 B per thread, kMT x 128 B per tile): shared by the ncol column tiles
+  // of the head, each taking kMT / ncol rows, loaded now so that their latency passes under the
+  // operand loads, stored at the end
+  bf16x8 rope_v;
+  int64_t rope_dst = -1;
+  if (rope != nullptr) {
+    const int rows = kMT / ncol, ct = nb / 128;
+    if (tid < 8 * rows) {
+      const int m = m0 + ct * rows + (tid >> 3), ch = tid & 7;
+      if (m < T) {
+        rope_v = *reinterpret_cast<const bf16x8*>(rope + ((int64_t)m * H + h) * 64 + 8 * ch);
+        rope_dst = ((int64_t)m * H + h) * ldc + N + 8 * ch;
+      }
+    }
+  }
   f32x16 acc[kRB];
 #pragma unroll
   for (int i = 0; i < kRB; ++i)
@@ -182,20 +198,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
         static_cast<float*>(C)[((int64_t)m * H + h) * ldc + n0 + l32] = acc[i][r];
       }
   }
-  if (rope != nullptr && nb == 0) {
-    // kMT rows x 64 rope values (128 B per row): one 16-B chunk per thread and pass
-#pragma unroll
-    for (int s2 = 0; s2 < kMT * 8 / kProjThreads; ++s2) {
-      const int k = tid + kProjThreads * s2;
-      const int rr = k >> 3, ch = k & 7;
-      const int m = m0 + rr;
-      if (m < T) {
-        const int64_t src = ((int64_t)m * H + h) * 64 + 8 * ch;
-        const int64_t dst = ((int64_t)m * H + h) * ldc + N + 8 * ch;
-        *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(C) + dst) = *reinterpret_cast<const bf16x8*>(rope + src);
-      }
-    }
-  }
+  if (rope_dst >= 0) *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(C) + rope_dst) = rope_v;
 }
 
 constexpr int proj_lds_bytes(bool a_float, bool db, int mt) {
