@@ -28,6 +28,7 @@ constexpr int kProjThreads = 256;
 constexpr int kProjKc = 128;                  // k per chunk
 constexpr int kProjBBytes = 128 * kProjKc * 2;   // B block: 128 rows x 128 k, bf16 (32 KiB)
 constexpr int kProjSmallTokens = 64;             // up to this many tokens: 32-token tiles
+constexpr int kAbsorbTile = 32;                  // absorption token tile above that (32: 1-4% faster than 64)
 
 // LDS-DMA of a block of `rows` rows x kProjKc elements of `esz` bytes from a row-major source
 // (row stride `src_stride` bytes, block start at byte `src0` of the buffer): LDS holds row r at
@@ -201,6 +202,100 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const void* __restri
   if (rope_dst >= 0) *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(C) + rope_dst) = rope_v;
 }
 
+// Query absorption for many tokens: one work-group per (head, 128-column tile, token share).
+// Each wave keeps its 32 weight columns (all 128 k) in 32 VGPRs for the whole work-group, so
+// the weight block is read once per work-group; the work-group then walks its token tiles of
+// kMT rows (tiles split, split + S, ...), staging each q_nope tile in LDS by LDS-DMA and
+// writing the bf16 output through LDS as 16-B row stores (as in proj_kernel). LDS is only the
+// operand tile and the output tile (2 x kMT x 256 B), so several work-groups share a CU and
+// cover each other's load and store latencies. The S token shares of one (head, column tile)
+// and the four column tiles of a head (which read the same q_nope rows) share a block-index
+// residue mod 8, hence an XCD and its L2. The head's rope rows are copied by its four column
+// tiles, a quarter of each token tile each.
+template <int kMT>
+__global__ __launch_bounds__(kProjThreads) void absorb_tiles_kernel(const __bf16* __restrict__ A,
+                                                                    const __bf16* __restrict__ B,
+                                                                    __bf16* __restrict__ C,
+                                                                    const __bf16* __restrict__ rope, int T, int H,
+                                                                    int S) {
+  static_assert(kMT == 32 || kMT == 64 || kMT == 128, "token tile");
+  constexpr int kRB = kMT / 32;
+  constexpr int K = kNope, N = kLat, ldc = kDqk;
+  constexpr uint32_t kOut = kMT * 256;   // output tile after the operand tile
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  char __attribute__((address_space(3)))* lds = (char __attribute__((address_space(3)))*)smem_raw;
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int lin = blockIdx.x, x8 = lin & 7, r = lin >> 3;
+  const int ct = r & 3, split = (r >> 2) % S, h = (r / (4 * S)) * 8 + x8;
+  if (h >= H) return;
+  const int nb = 128 * ct, ntile = (T + kMT - 1) / kMT;
+  // this lane's weight fragments: row nb + 32 wave + l32 of W_k[h], k 16j + 8hh .. +7
+  bf16x8 bfr[8];
+  {
+    const __bf16* wrow = B + ((int64_t)h * N + nb + 32 * wave + l32) * K + 8 * hh;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(wrow + 16 * j);
+  }
+  const i32x4 ra = make_rsrc(reinterpret_cast<uint64_t>(A), (int)((int64_t)T * H * K * 2));
+#pragma unroll 1
+  for (int it = split; it < ntile; it += S) {
+    const int m0 = kMT * it;
+    stage_block(ra, lds_u32, (uint32_t)(((int64_t)m0 * H + h) * K) * 2, (uint32_t)H * K * 2, kMT, 2, tid);
+    // this column tile's quarter of the tile's rope rows: 16 B per thread
+    bf16x8 rope_v;
+    int64_t rope_dst = -1;
+    if (tid < 2 * kMT) {
+      const int m = m0 + ct * (kMT / 4) + (tid >> 3), ch = tid & 7;
+      if (m < T) {
+        rope_v = *reinterpret_cast<const bf16x8*>(rope + ((int64_t)m * H + h) * 64 + 8 * ch);
+        rope_dst = ((int64_t)m * H + h) * ldc + N + 8 * ch;
+      }
+    }
+    wait_vmcnt<0>();
+    barrier_lds();
+    f32x16 acc[kRB];
+#pragma unroll
+    for (int i = 0; i < kRB; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = 2 * j + hh;
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) {
+        const bf16x8 af = lds_b128(lds + ((uint32_t)(32 * i + l32) * 256u + 16u * (uint32_t)(c ^ (l32 & 15))));
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af, acc[i], 0, 0, 0);
+      }
+    }
+    // acc[i] register 4q + v of lane l: token 32 i + l%32, column 32 wave + 8q + 4(l/32) + v
+#pragma unroll
+    for (int i = 0; i < kRB; ++i) {
+      const uint32_t t = (uint32_t)(32 * i + l32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[i][4 * q + e];
+        *(bf16x4 __attribute__((address_space(3)))*)(lds + (kOut + t * 256u +
+                                                            16u * (((uint32_t)(4 * wave + q)) ^ (t & 15u)) +
+                                                            8u * (uint32_t)hh)) = v;
+      }
+    }
+    barrier_lds();   // (also: every wave has read the operand tile before the next one is loaded)
+#pragma unroll
+    for (int s2 = 0; s2 < kMT * 16 / kProjThreads; ++s2) {
+      const int k = tid + kProjThreads * s2;
+      const int t = k >> 4, q = k & 15;
+      const int m = m0 + t;
+      const u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(lds + (kOut + t * 256 + 16 * (q ^ (t & 15))));
+      if (m < T) *reinterpret_cast<u32x4*>(C + ((int64_t)m * H + h) * ldc + nb + 8 * q) = v;
+    }
+    if (rope_dst >= 0) *reinterpret_cast<bf16x8*>(C + rope_dst) = rope_v;
+  }
+}
+
 constexpr int proj_lds_bytes(bool a_float, bool db, int mt) {
   return (db ? 2 : 1) * (kProjBBytes + mt * kProjKc * (a_float ? 4 : 2));
 }
@@ -242,8 +337,20 @@ hipError_t decompress_launch(const float* out_latent, const void* w_v, int token
 
 hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const void* w_k, int tokens, int heads,
                                void* qz, hipStream_t stream) {
-  if (tokens <= kProjSmallTokens) absorb_launch<32>(q_nope, q_rope, w_k, tokens, heads, qz, stream);
-  else absorb_launch<128>(q_nope, q_rope, w_k, tokens, heads, qz, stream);
+  if (tokens <= kProjSmallTokens) {
+    absorb_launch<32>(q_nope, q_rope, w_k, tokens, heads, qz, stream);
+  } else {
+    // token shares per (head, column tile): enough work-groups for about four per CU
+    constexpr int kMT = kAbsorbTile;
+    const int ntile = (tokens + kMT - 1) / kMT;
+    const int pairs = 4 * heads;
+    int S = (1024 + pairs - 1) / pairs;
+    S = S < 1 ? 1 : (S > ntile ? ntile : S);
+    const dim3 grid(8 * 4 * S * ((heads + 7) / 8));
+    hipLaunchKernelGGL(absorb_tiles_kernel<kMT>, grid, dim3(kProjThreads), 2 * kMT * 256, stream,
+                       static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(w_k), static_cast<__bf16*>(qz),
+                       static_cast<const __bf16*>(q_rope), tokens, heads, S);
+  }
   return hipGetLastError();
 }
 
