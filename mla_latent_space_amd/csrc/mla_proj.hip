@@ -296,6 +296,104 @@ __global__ __launch_bounds__(kProjThreads) void absorb_tiles_kernel(const __bf16
   }
 }
 
+// Output decompression for many tokens: one work-group per (head, token share). Each wave keeps
+// its 32 output columns of W_v[h] over all 512 k in 128 VGPRs for the whole work-group, so the
+// weights are read once per work-group; the fp32 O_latent rows of each 32-token tile stream
+// through LDS in four 128-k chunks of 16 KiB by LDS-DMA, kDecAhead chunks ahead of the one
+// multiplied (kDecAhead + 1 buffers). The waits count exactly what is younger than the chunk
+// awaited: the later chunks' DMA instructions (issued for every chunk position, with zero
+// records past the work-group's last chunk) and, for the first kDecAhead chunks of a tile, the
+// previous tile's output stores, which are range-checked buffer stores (rows past the last
+// token are dropped by the buffer's record count) so that every wave issues exactly 16 of them
+// per tile. The S token shares of a head share a block-index residue mod 8, hence an XCD and
+// the L2 that serves their weight reads.
+constexpr int kDecAhead = 3;
+__global__ __launch_bounds__(kProjThreads) void decompress_tiles_kernel(const float* __restrict__ A,
+                                                                        const __bf16* __restrict__ B,
+                                                                        float* __restrict__ C, int T, int H, int S) {
+  constexpr int K = kLat, N = kDv, kMT = 32;
+  constexpr uint32_t kChunk = kMT * kProjKc * 4;          // 16 KiB of fp32 rows
+  constexpr int kBufs = kDecAhead + 1;
+  constexpr int kDmaW = kChunk / 1024 / 4;                // LDS-DMA instructions per wave and chunk
+  constexpr int kStores = 16;                             // output stores per wave and tile
+  static_assert(kDmaW * 4 * 1024 == (int)kChunk && (kDecAhead * kDmaW + kStores) < 64, "wait counts");
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  char __attribute__((address_space(3)))* lds = (char __attribute__((address_space(3)))*)smem_raw;
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int lin = blockIdx.x, x8 = lin & 7, r = lin >> 3;
+  const int split = r % S, h = (r / S) * 8 + x8;
+  const int ntile = (T + kMT - 1) / kMT;
+  if (h >= H || split >= ntile) return;
+  const int nchunks = 4 * ((ntile - split + S - 1) / S);
+  // this lane's weight fragments: row 32 wave + l32 of W_v[h] (512 k), k 16j + 8hh .. +7
+  bf16x8 bfr[32];
+  {
+    const __bf16* wrow = B + ((int64_t)h * N + 32 * wave + l32) * K + 8 * hh;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(wrow + 16 * j);
+  }
+  const i32x4 ra = make_rsrc(reinterpret_cast<uint64_t>(A), (int)((int64_t)T * H * K * 4));
+  const i32x4 rnone = make_rsrc(reinterpret_cast<uint64_t>(A), 0);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(C, (short)0, (int)((int64_t)T * H * N * 4),
+                                                                      (int)kRsrcWord3);
+  auto issue = [&](int g) {
+    const uint32_t dst = lds_u32 + (uint32_t)(g % kBufs) * kChunk;
+    const int tile = split + S * (g >> 2);
+    const uint32_t src = (uint32_t)(((int64_t)kMT * tile * H + h) * K + 128 * (g & 3)) * 4u;
+    stage_block(g < nchunks ? ra : rnone, dst, g < nchunks ? src : 0u, (uint32_t)H * K * 4, kMT, 4, tid);
+  };
+#pragma unroll
+  for (int g = 0; g < kDecAhead; ++g) issue(g);
+#pragma unroll 1
+  for (int tl = 0; tl < nchunks / 4; ++tl) {
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {   // (unrolled: the weight fragments are indexed by c at compile time)
+      const int g = 4 * tl + c;
+      issue(g + kDecAhead);
+      if (c < kDecAhead && tl > 0) wait_vmcnt<kDecAhead * kDmaW + kStores>();
+      else wait_vmcnt<kDecAhead * kDmaW>();
+      barrier_lds();
+      const uint32_t buf = (uint32_t)(g % kBufs) * kChunk;
+#pragma unroll
+      for (int j = 0; j < kProjKc / 16; ++j) {
+        const int cc = 2 * j + hh;   // bf16 chunk of k 16j + 8hh: fp32 chunks 2cc, 2cc + 1 of the 512-B row
+        const f32x4 lo = *(const f32x4 __attribute__((address_space(3)))*)(
+            lds + (buf + l32 * 512 + 16 * ((2 * cc) ^ (l32 & 15))));
+        const f32x4 hi = *(const f32x4 __attribute__((address_space(3)))*)(
+            lds + (buf + l32 * 512 + 16 * ((2 * cc + 1) ^ (l32 & 15))));
+        bf16x8 af;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          af[q] = (__bf16)lo[q];
+          af[4 + q] = (__bf16)hi[q];
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[8 * c + j], acc, 0, 0, 0);
+      }
+      barrier_lds();   // this chunk's buffer is read before it is loaded again
+    }
+    // acc register q of lane l: row m0 + 8(q/4) + 4(l/32) + q%4, column 32 wave + l%32
+    const int m0 = kMT * (split + S * tl);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int m = m0 + 8 * (q >> 2) + 4 * hh + (q & 3);
+      const uint32_t off = (uint32_t)(((int64_t)m * H + h) * N + 32 * wave + l32) * 4u;
+      // (the value is moved to a plain VGPR first: taken straight from the accumulator vector, the
+      // store builtin was compiled to store its first element for every q)
+      float v = acc[q];
+      asm volatile("" : "+v"(v));
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, (int)off, 0, 0);
+    }
+  }
+  // the trailing zero-record DMAs land in LDS before the work-group ends (the last stores may
+  // stay in flight)
+  wait_vmcnt<kStores>();
+}
+
 constexpr int proj_lds_bytes(bool a_float, bool db, int mt) {
   return (db ? 2 : 1) * (kProjBBytes + mt * kProjKc * (a_float ? 4 : 2));
 }
@@ -356,9 +454,22 @@ hipError_t launch_absorb_query(const void* q_nope, const void* q_rope, const voi
 
 hipError_t launch_decompress_output(const float* out_latent, const void* w_v, int tokens, int heads, float* out,
                                     hipStream_t stream) {
-  const hipError_t e = tokens <= kProjSmallTokens ? decompress_launch<32>(out_latent, w_v, tokens, heads, out, stream)
-                                                   : decompress_launch<64>(out_latent, w_v, tokens, heads, out, stream);
-  if (e != hipSuccess) return e;
+  // token shares per head for decompress_tiles_kernel: enough work-groups for about two per CU;
+  // that kernel only pays when every work-group walks at least two tiles (each loads its head's
+  // 128 KiB of weights once)
+  const int ntile = (tokens + 31) / 32;
+  const int S = (512 + heads - 1) / heads;
+  if (tokens <= kProjSmallTokens) {
+    const hipError_t e = decompress_launch<32>(out_latent, w_v, tokens, heads, out, stream);
+    if (e != hipSuccess) return e;
+  } else if (ntile < 2 * S) {
+    const hipError_t e = decompress_launch<64>(out_latent, w_v, tokens, heads, out, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    const dim3 grid(8 * S * ((heads + 7) / 8));
+    hipLaunchKernelGGL(decompress_tiles_kernel, grid, dim3(kProjThreads), (kDecAhead + 1) * 32 * kProjKc * 4, stream,
+                       out_latent, static_cast<const __bf16*>(w_v), out, tokens, heads, S);
+  }
   return hipGetLastError();
 }
 

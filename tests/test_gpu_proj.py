@@ -45,7 +45,8 @@ def test_absorb_query_matches_oracle(tokens, heads):
         assert np.array_equal(got[t, :, 512:], ref[:, 512:]), f"token {t}: rope part not copied exactly"
 
 
-@pytest.mark.parametrize("tokens,heads", [(1, 16), (5, 32), (64, 128), (65, 16), (70, 16), (200, 16), (517, 8)])
+@pytest.mark.parametrize("tokens,heads", [(1, 16), (5, 32), (64, 128), (65, 16), (70, 16), (200, 16), (517, 8),
+                                           (300, 128), (2050, 16)])
 def test_decompress_output_matches_oracle(tokens, heads):
     """out within (2^-8 + 2^-14) sum |a w| of the exact product: O_latent is rounded to bf16 on
     load (unit roundoff 2^-8 per term) and 512 terms are accumulated in fp32 (below 2^-14)."""
