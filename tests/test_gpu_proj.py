@@ -23,7 +23,7 @@ def _bf16(shape, gen, scale=1.0):
 
 
 @pytest.mark.parametrize("tokens,heads", [(1, 16), (3, 16), (37, 32), (64, 128), (65, 16), (100, 64), (300, 16),
-                                           (517, 8)])
+                                           (517, 8), (100, 12)])
 def test_absorb_query_matches_oracle(tokens, heads):
     """Qz nope part within the bf16 rounding of the exact value (unit roundoff 2^-8) plus the
     fp32 accumulation error (<= 2^-20 sum |q w| for 128 terms); the rope part copied bit for
@@ -46,7 +46,7 @@ def test_absorb_query_matches_oracle(tokens, heads):
 
 
 @pytest.mark.parametrize("tokens,heads", [(1, 16), (5, 32), (64, 128), (65, 16), (70, 16), (200, 16), (517, 8),
-                                           (300, 128), (2050, 16)])
+                                           (300, 128), (2050, 16), (2760, 12)])
 def test_decompress_output_matches_oracle(tokens, heads):
     """out within (2^-8 + 2^-14) sum |a w| of the exact product: O_latent is rounded to bf16 on
     load (unit roundoff 2^-8 per term) and 512 terms are accumulated in fp32 (below 2^-14)."""
